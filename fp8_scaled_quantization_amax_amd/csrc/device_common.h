@@ -1,0 +1,145 @@
+// Device-side helpers shared by the fp8q HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8q.h"
+#include "launch.h"
+
+namespace fp8q {
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+constexpr float kScaleFloor = 1e-12f;  // clamp_min of the lab page's scaled_roundtrip
+
+template <int FMT>
+__device__ __forceinline__ constexpr float fmt_max() { return FMT == FP8Q_E4M3 ? kE4M3Max : kE5M2Max; }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// s = max(RN32(amax / fmax), RN32(1e-12)), NaN-propagating.  The quotient uses
+// the compiler's IEEE (correctly rounded) fp32 division.
+template <int FMT>
+__device__ __forceinline__ float scale_from_amax(float amax) {
+    const float s = amax / fmt_max<FMT>();
+    if (s != s) return s;
+    return s < kScaleFloor ? kScaleFloor : s;
+}
+
+// Correctly rounded fp32 quotient x / s for a positive scale s, given
+// r = RN32(1 / s).  q0 = x*r is within about 2 ulp; one FMA residual step
+// makes it faithful; a second gives the correctly rounded quotient
+// (Markstein's theorem: a faithful quotient corrected by the exact FMA
+// residual times a correctly rounded reciprocal rounds correctly; see Muller
+// et al., Handbook of Floating-Point Arithmetic, chapter on division with an
+// FMA).  Non-finite q0 (x non-finite, or |x/s| beyond fp32) is returned as is:
+// every such quotient encodes to the overflow / NaN code either way.  The
+// sign is restored at the end because the residual steps turn -0 into +0.
+__host__ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+    const float q0 = x * r;
+    if (!(__builtin_fabsf(q0) <= 3.402823466e38f)) return q0;
+    float e = __builtin_fmaf(-q0, s, x);
+    const float q1 = __builtin_fmaf(e, r, q0);
+    e = __builtin_fmaf(-q1, s, x);
+    const float q2 = __builtin_fmaf(e, r, q1);
+    return __builtin_copysignf(q2, x);
+}
+
+// Optional saturation: |v| > fmax -> +-fmax (NaN unchanged).
+template <int FMT, bool SAT>
+__device__ __forceinline__ float saturate(float v) {
+    if constexpr (SAT) {
+        return __builtin_fabsf(v) > fmt_max<FMT>() ? __builtin_copysignf(fmt_max<FMT>(), v) : v;
+    } else {
+        return v;
+    }
+}
+
+// Four fp32 values -> four 8-bit codes packed little-endian in a dword.  The
+// gfx950 conversions round to nearest even and, without clamping, overflow
+// E4M3 to NaN and E5M2 to Inf (checked exhaustively against the definition
+// on every fp32 input).
+template <int FMT>
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+    int w = 0;
+    if constexpr (FMT == FP8Q_E4M3) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, w, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    }
+    return (uint32_t)w;
+}
+
+// |x| as an ordered integer key: NaN patterns sort above +Inf, so an integer
+// max over keys is a NaN-propagating amax.
+__device__ __forceinline__ uint32_t abs_key(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Max over lanes whose index differs only in the bits of `mask` (a power-of-two run).
+template <int LO, int HI>
+__device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = LO; off <= HI; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Block-wide max of a per-thread key (blockDim.x == 256).  Uses 4 words of LDS.
+__device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* lds4) {
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) lds4[wave] = v;
+    __syncthreads();
+    uint32_t r = lds4[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) r = r > lds4[i] ? r : lds4[i];
+    __syncthreads();
+    return r;
+}
+
+// Reduce the partial maxima written by the amax grid (one float per block).
+__device__ __forceinline__ float reduce_partials_256(const float* partials, int nparts, uint32_t* lds4) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) {
+        const uint32_t k = abs_key(partials[i]);
+        m = m > k ? m : k;
+    }
+    return __uint_as_float(block_max_u32_256(m, lds4));
+}
+
+// E8M0 exponent for an MX block: e = ceil(log2 s) read from the bits of the
+// (positive, normal) scale s; returns 255 for a non-finite s.
+__device__ __forceinline__ int e8m0_from_scale(float s) {
+    if (!(s <= 3.402823466e38f)) return 255;
+    const uint32_t b = __float_as_uint(s);
+    const int be = (int)(b >> 23);
+    return ((b & 0x7fffffu) == 0 ? be - 127 : be - 126) + 127;
+}
+
+// 2^(127 - code) as fp32 (the exact reciprocal of an E8M0 scale), NaN for 255.
+__device__ __forceinline__ float e8m0_recip(int code) {
+    if (code == 255) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((uint32_t)(254 - code) << 23);
+}
+
+// bf16 round to nearest even of an fp32 value (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    const uint32_t b = __float_as_uint(f);
+    if ((b & 0x7fffffffu) > 0x7f800000u) return (b >> 16) | 0x40u;
+    return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+}  // namespace fp8q

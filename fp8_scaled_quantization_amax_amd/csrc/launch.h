@@ -1,0 +1,80 @@
+// Host-side launchers of the fp8q HIP kernels (internal; the C ABI is in fp8q.h).
+// Launchers assume validated arguments and return the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8q.h"
+
+namespace fp8q {
+
+// Largest number of blocks a reduction grid uses; the reduce workspace holds
+// one fp32 partial maximum per block.
+constexpr int kReduceParts = 1024;
+constexpr size_t kReduceWsBytes = kReduceParts * sizeof(float);
+
+// Quantization schemes of the tiled quantize kernel.
+enum Scheme : int {
+    kPerTensorCurrent = 0,  // s from the amax partials of a preceding amax grid
+    kPerTensorDelayed = 1,  // s from the amax history (cold start: partials)
+    kTileAxis0 = 2,         // 1 x 128 along columns
+    kTileAxis1 = 3,         // 128 x 1 along rows
+    kBlock = 4,             // 128 x 128
+    kMxAxis0 = 5,           // 1 x 32 along columns, E8M0
+    kMxAxis1 = 6            // 32 x 1 along rows, E8M0
+};
+
+struct QuantArgs {
+    const void* x;
+    int hp;
+    int64_t rows, cols;
+    int fmt;
+    int scheme;
+    bool saturate;
+    uint8_t* q;            // [rows, cols] or NULL
+    uint8_t* qT;           // [cols, rows] or NULL
+    float* scales;         // tile / block scales
+    uint8_t* e8m0;         // MX scales
+    const float* partials; // amax partials (per-tensor current; delayed cold start)
+    int nparts;
+    fp8q_delayed_state* state;
+    float* scale_out;
+    float* amax_out;
+};
+
+// amax partial maxima over n elements: one float per block into partials[0..nparts).
+// If gate != NULL the grid does nothing unless gate's history is all zero.
+// Returns the number of partials written (the grid size).
+int amax_partials_grid(int64_t n);
+hipError_t launch_amax_partials(const void* x, int hp, int64_t n, float* partials, int nparts,
+                                const fp8q_delayed_state* gate, hipStream_t s);
+hipError_t launch_amax_finalize(const float* partials, int nparts, float* amax_out, hipStream_t s);
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+// codes [rows, cols] -> [cols, rows]
+hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out, hipStream_t s);
+
+// Scaled GEMM on K-contiguous codes: C[M,N] = sum_k A[m,k] B[n,k] with scales.
+struct GemmScale {
+    const void* s;     // float* or uint8_t* (E8M0)
+    int gran;          // fp8q_gran
+    int64_t ld;        // row stride of the scale array (elements)
+    int64_t kstride;   // stride between K blocks (elements)
+    int rshift;        // operand row -> scale row: row >> rshift (0: per row, 7: 128-row blocks)
+};
+
+struct GemmArgs {
+    const uint8_t* A;  // [M, K]
+    const uint8_t* B;  // [N, K]
+    void* C;           // [M, N]
+    int64_t M, N, K;
+    int fa, fb;        // fp8q_format
+    int c_dtype;       // fp8q_hp
+    GemmScale sa, sb;
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+
+}  // namespace fp8q

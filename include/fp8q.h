@@ -1,0 +1,262 @@
+/*
+ * fp8q: dynamic FP8 scaling and the scaled FP8 GEMM on AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a DEVICE pointer unless stated otherwise,
+ * and every call enqueues its work on `stream` (a hipStream_t; NULL is the
+ * null stream) and returns without synchronising.  Arguments are validated on
+ * the host before any HIP call: a call that returns an error has enqueued
+ * nothing and changed nothing.  The library allocates no device memory and
+ * keeps no state between calls except a per-device cache of the device
+ * architecture; buffers (including workspaces and delayed-scaling state) are
+ * owned by the caller.  Outputs must not alias inputs.  No call ever falls
+ * back to another precision or another algorithm: an unsupported request is
+ * an error (FP8Q_EUNSUPPORTED).
+ *
+ * What the operations compute (page citations name the source page and its
+ * section):
+ *   amax      max |x_i|, NaN-propagating.  "fp8_parity.py" lab page,
+ *             scaled_roundtrip (x.abs().max()).
+ *   scale     s = max(amax / fmax, 1e-12) in fp32, fmax = 448 (E4M3) or
+ *             57344 (E5M2).  Same function; constants E4M3_MAX / E5M2_MAX.
+ *   cast      q_i = RNE_fp8(RN_fp32(x_i / s)), OCP float8_e4m3fn / float8_e5m2,
+ *             non-saturating (E4M3 overflow -> NaN, E5M2 -> Inf) unless
+ *             FP8Q_SATURATE.  Same function, (x / scale).to(dtype); smoke
+ *             check [2] fixes the overflow rule.
+ *   delayed   s from the maximum of an amax history of earlier steps (16
+ *             entries); the current amax is recorded afterwards.  Smoke
+ *             check [3]; SpikingJelly "Training and Inference Precision",
+ *             recipe "delayed".
+ *   granular  one scale per 1x128 tile (smoke check [4]), per 128x128 block
+ *             (SpikingJelly recipe "block"; "How to Optimize
+ *             Transformer-Based Models for Low-Precision Training", 2D block
+ *             scaling of weights) or one power-of-two E8M0 scale per 32
+ *             elements (recipe "mxfp8").
+ *   GEMM      y = (Aq . Bq) * sA * sB with fp32 accumulation; fprop (NT),
+ *             dgrad (NN), wgrad (TN).  Lab page, class FP8Matmul (forward
+ *             xq @ wq.T, backward gq @ wq and gq.T @ xq); the blog post's
+ *             fprop / dgrad / wgrad shapes and its autocast vs pre-quantize
+ *             modes.
+ *
+ * Layouts: all matrices are row-major and dense (row stride = columns).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+typedef enum fp8q_status {
+    FP8Q_OK = 0,
+    FP8Q_EINVAL = 1,       /* null pointer, negative or zero size, unknown enum or flag */
+    FP8Q_EALIGN = 2,       /* a dimension is not a multiple of what the operation needs */
+    FP8Q_EUNSUPPORTED = 3, /* a valid combination this library does not implement */
+    FP8Q_EDEVICE = 4,      /* no HIP device, or the current device is not gfx950 */
+    FP8Q_ELAUNCH = 5,      /* a HIP launch failed (message in fp8q_last_error) */
+    FP8Q_EWORKSPACE = 6    /* workspace missing or smaller than required */
+} fp8q_status;
+
+/* 8-bit formats: OCP float8_e4m3fn (max 448) and float8_e5m2 (max 57344). */
+typedef enum fp8q_format { FP8Q_E4M3 = 0, FP8Q_E5M2 = 1 } fp8q_format;
+
+/* High-precision element types: IEEE fp32 and bfloat16. */
+typedef enum fp8q_hp { FP8Q_F32 = 0, FP8Q_BF16 = 1 } fp8q_hp;
+
+/* Scale granularity. */
+typedef enum fp8q_gran {
+    FP8Q_PER_TENSOR = 0,    /* one fp32 scale */
+    FP8Q_TILE_1x128 = 1,    /* one fp32 scale per 128 consecutive elements along K */
+    FP8Q_BLOCK_128x128 = 2, /* one fp32 scale per 128 x 128 block */
+    FP8Q_MX32 = 3           /* one E8M0 scale (2^(code-127)) per 32 elements along K */
+} fp8q_gran;
+
+/* Per-tensor scaling mode. */
+typedef enum fp8q_scaling { FP8Q_CURRENT = 0, FP8Q_DELAYED = 1 } fp8q_scaling;
+
+/* Flags. */
+#define FP8Q_SATURATE 1u   /* clamp finite and infinite overflow to +-fmax instead of NaN / Inf */
+
+#define FP8Q_HISTORY_LEN 16
+
+/*
+ * Delayed-scaling state, in DEVICE memory, owned by the caller.  Create it
+ * zero-filled (an all-zero history is a cold start, which uses the current
+ * amax).  amax_bits and arrive are the library's working fields; every call
+ * leaves them zero.  One state must not be used by two calls that may run
+ * concurrently.  Saving amax_history and pos checkpoints the recipe.
+ */
+typedef struct fp8q_delayed_state {
+    float amax_history[FP8Q_HISTORY_LEN]; /* amaxes of earlier steps (ring) */
+    int32_t pos;                          /* next ring slot to write */
+    uint32_t amax_bits;                   /* working field, zero between calls */
+    uint32_t arrive;                      /* working field, zero between calls */
+    float last_scale;                     /* scale used by the most recent call */
+} fp8q_delayed_state;
+
+/* ---------------------------------------------------------------- misc */
+
+/* FP8Q_ABI_VERSION of the loaded library. */
+int fp8q_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* fp8q_status_string(int status);
+
+/* Detail of the most recent failed call on this host thread ("" if none).
+ * The string stays valid until the next call on this thread. */
+const char* fp8q_last_error(void);
+
+/* Bytes of device workspace the reductions need (amax partial maxima). */
+size_t fp8q_reduce_workspace_bytes(void);
+
+/* ---------------------------------------------------------------- amax */
+
+/*
+ * amax_out[0] = max_i |x_i| over n elements of type hp (NaN if any x_i is
+ * NaN).  x: n elements, any alignment of the element type.  ws: at least
+ * fp8q_reduce_workspace_bytes() bytes of scratch (contents ignored and
+ * overwritten).  Lab page, scaled_roundtrip: x.abs().max().
+ */
+int fp8_amax(const void* x, int hp, int64_t n, float* amax_out,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- quantize */
+
+/*
+ * Per-tensor quantization of x [rows, cols] (type hp) to codes q [rows, cols]
+ * in format fmt.
+ *   scaling = FP8Q_CURRENT: s = max(amax(x)/fmax, 1e-12) (two passes over x).
+ *   scaling = FP8Q_DELAYED: s = max(max(history)/fmax, 1e-12) from `state`
+ *     (cold start: current amax); one pass casts and measures amax(x), which
+ *     is then written to history[pos] and pos advances modulo 16.
+ * qT: optional (may be NULL) second copy of the codes transposed, [cols, rows]
+ *   (the K-major operand of a dgrad or wgrad GEMM).
+ * scale_out: required, receives s.  amax_out: optional, receives amax(x).
+ * flags: 0 or FP8Q_SATURATE.  ws: fp8q_reduce_workspace_bytes() bytes.
+ * state: required for DELAYED, ignored for CURRENT.
+ * Lab page: scaled_roundtrip; smoke check [3] (delayed vs current).
+ */
+int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols,
+                            int fmt, int scaling, fp8q_delayed_state* state,
+                            uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
+                            unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * 1x128 tile quantization with fp32 scales (lab page smoke check [4]).
+ *   axis = 0: tiles of 128 consecutive columns of a row;
+ *             scales [rows, ceil(cols/128)].
+ *   axis = 1: tiles of 128 consecutive rows of a column (the 128x1 tiles a
+ *             wgrad operand needs, whose contraction runs over rows);
+ *             scales [cols, ceil(rows/128)].
+ * A tile at the end of a row or column may be shorter.  q [rows, cols];
+ * qT optional [cols, rows].  Each tile: s = max(amax(tile)/fmax, 1e-12).
+ */
+int fp8_quantize_tile1x128(const void* x, int hp, int64_t rows, int64_t cols, int axis,
+                           int fmt, uint8_t* q, uint8_t* qT, float* scales,
+                           unsigned flags, void* stream);
+
+/*
+ * 128x128 block quantization with fp32 scales [ceil(rows/128), ceil(cols/128)]
+ * (weights; SpikingJelly recipe "block", blog: 2D block scaling for weights).
+ * q [rows, cols]; qT optional [cols, rows].
+ */
+int fp8_quantize_block128x128(const void* x, int hp, int64_t rows, int64_t cols,
+                              int fmt, uint8_t* q, uint8_t* qT, float* scales,
+                              unsigned flags, void* stream);
+
+/*
+ * MX32 quantization: one E8M0 byte per 32 elements (SpikingJelly recipe
+ * "mxfp8").  Scale 2^e with e = ceil(log2(max(amax/fmax, 1e-12))) so that no
+ * scaled element exceeds fmax; E8M0 code = e + 127 (255 if the block holds a
+ * NaN or Inf).  axis and layouts as fp8_quantize_tile1x128 with 32 in place
+ * of 128: e8m0 [rows, ceil(cols/32)] (axis 0) or [cols, ceil(rows/32)] (axis 1).
+ */
+int fp8_quantize_mx32(const void* x, int hp, int64_t rows, int64_t cols, int axis,
+                      int fmt, uint8_t* q, uint8_t* qT, uint8_t* e8m0,
+                      unsigned flags, void* stream);
+
+/* ---------------------------------------------------------------- GEMM */
+
+/*
+ * One GEMM operand.
+ *
+ * Pre-quantized (quantized = 1): `data` holds uint8 codes in the operand's
+ * stored layout for the operation (see the GEMM entry points) and `scale`
+ * holds its scales:
+ *   PER_TENSOR     float[1]
+ *   TILE_1x128     float [R, K/128], R = M for A and N for B, indexed by
+ *                  (operand row, K block) -- what fp8_quantize_tile1x128
+ *                  produces with its tiles running along K (axis 0 when K is
+ *                  the stored column axis, axis 1 when K is the stored row axis)
+ *   BLOCK_128x128  float [ceil(stored rows/128), ceil(stored cols/128)] in the
+ *                  operand's STORED layout (one weight array serves fprop and dgrad)
+ *   MX32           uint8 E8M0 [R, K/32], indexed like TILE_1x128
+ *   `data_kmajor` optionally holds the same codes already laid out [R, K]
+ *   (K contiguous); if NULL and the stored layout is not K-contiguous, the
+ *   library transposes the codes into the workspace.
+ * Autocast (quantized = 0): `data` holds fp32 or bf16 values (`hp`) in the
+ *   stored layout; the GEMM quantizes them itself with `granularity`
+ *   (PER_TENSOR with `scaling` CURRENT or DELAYED + `state`, or TILE_1x128 /
+ *   BLOCK_128x128 / MX32 with current scaling) into the workspace, inside the
+ *   same enqueued work, and writes the per-tensor scale / amax to
+ *   scale_out / amax_out when they are not NULL.
+ */
+typedef struct fp8q_operand {
+    const void* data;
+    const void* data_kmajor;
+    const void* scale;
+    int32_t quantized;
+    int32_t format;       /* fp8q_format */
+    int32_t granularity;  /* fp8q_gran */
+    int32_t hp;           /* fp8q_hp (autocast) */
+    int32_t scaling;      /* fp8q_scaling (autocast, per-tensor) */
+    uint32_t flags;       /* FP8Q_SATURATE (autocast) */
+    fp8q_delayed_state* state;
+    float* scale_out;
+    float* amax_out;
+} fp8q_operand;
+
+/*
+ * Workspace bytes a GEMM call with these arguments needs (0 if none).
+ * op: 0 = NT, 1 = NN, 2 = TN.  Returns (size_t)-1 for invalid arguments.
+ */
+size_t fp8_gemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
+                                const fp8q_operand* A, const fp8q_operand* B);
+
+/*
+ * C [M, N] = sum_k A(m,k) * B(n,k), with each product's operands' scales
+ * applied per the granularity (per-tensor: the sum times sA * sB; 1x128 /
+ * 128x128: per 128-element K block; MX32: per 32-element K block), fp32
+ * accumulation, C written as c_dtype (FP8Q_F32 or FP8Q_BF16, round to
+ * nearest even).
+ *
+ *   fp8_gemm_scaled_NT (fprop, y = x w^T):  A stored [M, K], B stored [N, K]
+ *   fp8_gemm_scaled_NN (dgrad, dx = g w):   A stored [M, K], B stored [K, N]
+ *   fp8_gemm_scaled_TN (wgrad, dw = g^T x): A stored [K, M], B stored [K, N]
+ *
+ * Alignment: M, N, K multiples of 16 (SpikingJelly alignment rule, lab page
+ * module_filter_fn); K a multiple of 128 with TILE_1x128 / BLOCK_128x128
+ * operands and of 32 with MX32.  Granularities: A and B each PER_TENSOR,
+ * TILE_1x128 or BLOCK_128x128 in any combination, or both MX32.
+ * ws: fp8_gemm_workspace_bytes(...) bytes (may be NULL when that is 0).
+ */
+int fp8_gemm_scaled_NT(int64_t M, int64_t N, int64_t K, const fp8q_operand* A,
+                       const fp8q_operand* B, void* C, int c_dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+int fp8_gemm_scaled_NN(int64_t M, int64_t N, int64_t K, const fp8q_operand* A,
+                       const fp8q_operand* B, void* C, int c_dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+int fp8_gemm_scaled_TN(int64_t M, int64_t N, int64_t K, const fp8q_operand* A,
+                       const fp8q_operand* B, void* C, int c_dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -363,8 +363,15 @@ void orc_gemm(int64_t M, int64_t N, int64_t K,
 {
     const int frac = (fa == ORC_E4M3 ? 9 : 16) + (fb == ORC_E4M3 ? 9 : 16);
     const int64_t kblk = sa->kblk < sb->kblk ? sa->kblk : sb->kblk;
+    int64_t ia_tab[256], ib_tab[256];
+    int fa_tab[256], fb_tab[256];
     int64_t ri;
+    int c;
     (void)M;
+    for (c = 0; c < 256; ++c) {          /* integer value of every code, once per call */
+        fa_tab[c] = code_to_int((uint8_t)c, fa, &ia_tab[c]);
+        fb_tab[c] = code_to_int((uint8_t)c, fb, &ib_tab[c]);
+    }
 #pragma omp parallel for schedule(dynamic, 1)
     for (ri = 0; ri < nrows; ++ri) {
         const int64_t m = rows ? rows[ri] : ri;
@@ -379,10 +386,8 @@ void orc_gemm(int64_t M, int64_t N, int64_t K,
                 int64_t k;
                 for (k = k0; k < k1; ++k) {
                     const uint8_t ca = A[m * a_sm + k * a_sk], cb = B[n * b_sn + k * b_sk];
-                    int64_t ia, ib;
-                    const int fina = code_to_int(ca, fa, &ia), finb = code_to_int(cb, fb, &ib);
-                    if (fina && finb) {
-                        sum += (__int128)ia * (__int128)ib;
+                    if (fa_tab[ca] && fb_tab[cb]) {
+                        sum += (__int128)ia_tab[ca] * (__int128)ib_tab[cb];
                     } else {
                         const double p = orc_decode(ca, fa) * orc_decode(cb, fb);
                         if (isnan(p)) nan = 1;

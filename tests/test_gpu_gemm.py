@@ -1,0 +1,239 @@
+"""GPU parity of the scaled FP8 GEMMs (fprop NT, dgrad NN, wgrad TN) against
+the exact-integer CPU oracle, to the stated tolerance (fp32 output: 1e-3 of
+max|y|; bf16 output: 2^-7 of max|y|), for per-tensor, 1x128 / 128x128 block
+and MX32 scaling, pre-quantized and autocast operands, at small shapes with
+ragged tiles and at the full layer shapes on sampled rows."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_scaled_quantization_amax_amd as fq
+import oracle
+import workloads
+from gpu_util import announce, dev, gemm_close, host_input, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+Q = fq.GemmOperand.quantized
+AC = fq.GemmOperand.autocast
+GEMM = {"NT": fq.fp8_gemm_scaled_NT, "NN": fq.fp8_gemm_scaled_NN, "TN": fq.fp8_gemm_scaled_TN}
+OGEMM = {"NT": oracle.gemm_nt, "NN": oracle.gemm_nn, "TN": oracle.gemm_tn}
+
+
+def kcontig(op, which):
+    """Is operand `which` ('A' or 'B') of op stored with K contiguous?"""
+    return {"NT": (True, True), "NN": (True, False), "TN": (False, False)}[op][which == "B"]
+
+
+def quantize_pt(x, fmt, emit_t):
+    """Per-tensor quantization on the GPU and in the oracle (both from the same input)."""
+    q, qT, s, _ = fq.fp8_quantize_per_tensor(x.to(dev()), fmt, emit_t=emit_t)
+    oq, os_, _ = oracle.quantize_per_tensor(host_input(x), fmt)
+    assert s.item() == os_
+    return q, qT, s, oq.reshape(x.shape), os_
+
+
+# ------------------------------------------------------------------ tiny layer
+def test_tiny_layer_all_ops_fp32_out():
+    """X[512,32], W1[64,32], G[512,64]: fprop E4M3 x E4M3, dgrad E5M2 x E4M3,
+    wgrad E5M2^T x E4M3, fp32 accumulate and output; also the W2 fprop."""
+    announce("tiny layer")
+    X, W1, W2, G = workloads.tiny_layer()
+    qx, qxT, sx, oqx, osx = quantize_pt(X, fq.E4M3, True)
+    qw, qwT, sw, oqw, osw = quantize_pt(W1, fq.E4M3, True)
+    qg, qgT, sg, oqg, osg = quantize_pt(G, fq.E5M2, True)
+    S = oracle.Scale
+    y = fq.fp8_gemm_scaled_NT(512, 64, 32, Q(qx, fq.E4M3, sx), Q(qw, fq.E4M3, sw), torch.float32)
+    ry = oracle.gemm_nt(oqx, oqw, 0, 0, S("tensor", osx), S("tensor", osw))
+    assert gemm_close(y, ry, torch.float32)
+    for kmaj in (True, False):
+        dx = fq.fp8_gemm_scaled_NN(512, 32, 64, Q(qg, fq.E5M2, sg), Q(qw, fq.E4M3, sw, kmajor=qwT if kmaj else None),
+                                   torch.float32)
+        assert gemm_close(dx, oracle.gemm_nn(oqg, oqw, 1, 0, S("tensor", osg), S("tensor", osw)), torch.float32)
+        dw = fq.fp8_gemm_scaled_TN(64, 32, 512, Q(qg, fq.E5M2, sg, kmajor=qgT if kmaj else None),
+                                   Q(qx, fq.E4M3, sx, kmajor=qxT if kmaj else None), torch.float32)
+        assert gemm_close(dw, oracle.gemm_tn(oqg, oqx, 1, 0, S("tensor", osg), S("tensor", osx)), torch.float32)
+    # second layer: relu(y) quantized, times W2 [16, 64]
+    H = torch.relu(torch.from_numpy(ry.astype(np.float32)))
+    qh, _, sh, oqh, osh = quantize_pt(H, fq.E4M3, False)
+    qw2, _, sw2, oqw2, osw2 = quantize_pt(W2, fq.E4M3, False)
+    y2 = fq.fp8_gemm_scaled_NT(512, 16, 64, Q(qh, fq.E4M3, sh), Q(qw2, fq.E4M3, sw2), torch.float32)
+    assert gemm_close(y2, oracle.gemm_nt(oqh, oqw2, 0, 0, S("tensor", osh), S("tensor", osw2)), torch.float32)
+
+
+# ------------------------------------------------------------------ per-tensor, ragged shapes
+SHAPES = [(16, 16, 16), (528, 272, 1040), (256, 256, 128), (1040, 784, 272)]
+FMT_PAIRS = [(fq.E4M3, fq.E4M3), (fq.E5M2, fq.E4M3), (fq.E5M2, fq.E5M2)]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS)
+@pytest.mark.parametrize("op", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_per_tensor_prequantized(shape, op, fa, fb, out_dtype):
+    M, N, K = shape
+    announce("gemm per-tensor", op, shape, fa, fb, out_dtype)
+    A, B = workloads.gemm_operands(op, M, N, K, seed=100 + M + N + K)
+    qa, qaT, sa, oqa, osa = quantize_pt(A, fa, True)
+    qb, qbT, sb, oqb, osb = quantize_pt(B, fb, True)
+    ref = OGEMM[op](oqa, oqb, fa, fb, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb))
+    for use_kmajor in (False, True):
+        oa = Q(qa, fa, sa, kmajor=qaT if (use_kmajor and not kcontig(op, "A")) else None)
+        ob = Q(qb, fb, sb, kmajor=qbT if (use_kmajor and not kcontig(op, "B")) else None)
+        C = GEMM[op](M, N, K, oa, ob, out_dtype)
+        assert gemm_close(C, ref, out_dtype), use_kmajor
+
+
+@pytest.mark.parametrize("op", ["NT", "NN", "TN"])
+def test_autocast_current_equals_prequantized(op):
+    """Autocast (quantize inside the call) gives bitwise the same C as quantizing
+    first and calling the GEMM on the codes."""
+    M, N, K = 528, 400, 656
+    announce("autocast current", op)
+    A, B = workloads.gemm_operands(op, M, N, K, seed=7)
+    Ad, Bd = A.to(dev()), B.to(dev())
+    sa_out = torch.empty(1, device=dev())
+    amax_out = torch.empty(1, device=dev())
+    C1 = GEMM[op](M, N, K, AC(Ad, fq.E5M2, scale_out=sa_out, amax_out=amax_out), AC(Bd, fq.E4M3), torch.bfloat16)
+    qa, qaT, sa, oqa, osa = quantize_pt(A, fq.E5M2, True)
+    qb, qbT, sb, oqb, osb = quantize_pt(B, fq.E4M3, True)
+    C2 = GEMM[op](M, N, K, Q(qa, fq.E5M2, sa, kmajor=qaT if not kcontig(op, "A") else None),
+                  Q(qb, fq.E4M3, sb, kmajor=qbT if not kcontig(op, "B") else None), torch.bfloat16)
+    assert torch.equal(C1, C2)
+    assert sa_out.item() == osa and amax_out.item() == oracle.amax(host_input(A))
+    ref = OGEMM[op](oqa, oqb, 1, 0, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb))
+    assert gemm_close(C1, ref, torch.bfloat16)
+
+
+def test_autocast_delayed_spike_row_is_nan():
+    """Delayed scaling inside the GEMM: after 16 warm-up steps a 40-sigma spike
+    in A overflows (E4M3 NaN), so that output row is NaN; current scaling keeps it."""
+    M, K, N = 512, 1024, 256
+    announce("autocast delayed")
+    st = fq.DelayedState(dev())
+    ost = oracle.DelayedState()
+    _, B = workloads.attn_out_operands(M=M, K=K, N=N)
+    qb, _, sb, oqb, osb = quantize_pt(B, fq.E4M3, False)
+    for t, x, spike in workloads.delayed_steps(M=M, K=K, steps=17):
+        C = fq.fp8_gemm_scaled_NT(M, N, K, AC(x.to(dev()), fq.E4M3, scaling=fq.DELAYED, state=st),
+                                  Q(qb, fq.E4M3, sb), torch.bfloat16)
+        oqa, osa, _ = oracle.quantize_delayed(host_input(x), fq.E4M3, ost)
+        ref = oracle.gemm_nt(oqa.reshape(M, K), oqb, 0, 0, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb))
+        assert gemm_close(C, ref, torch.bfloat16), t
+        if spike is not None:
+            Cn = C.float().cpu().numpy()
+            assert np.isnan(Cn[spike[0]]).all() and not np.isnan(np.delete(Cn, spike[0], 0)).any()
+            Cc = fq.fp8_gemm_scaled_NT(M, N, K, AC(x.to(dev()), fq.E4M3), Q(qb, fq.E4M3, sb), torch.bfloat16)
+            assert not torch.isnan(Cc).any()
+
+
+# ------------------------------------------------------------------ block-scaled and MX
+def block_operands(op, M, N, K, seed):
+    """Activation / gradient operand A with 1x128 tiles along K (128x1 for a
+    wgrad operand), weight-like operand B with 128x128 blocks (fprop, dgrad) or
+    128x1 tiles along K (wgrad)."""
+    A, B = workloads.gemm_operands(op, M, N, K, seed=seed, std=1.0, outlier_rows=0.01)
+    return A, B
+
+
+@pytest.mark.parametrize("op", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("shape", [(256, 128, 128), (528, 400, 640), (1024, 1536, 1024)])
+def test_block_scaled(op, shape):
+    M, N, K = shape
+    announce("gemm block-scaled", op, shape)
+    A, B = block_operands(op, M, N, K, seed=200 + M)
+    fa, fb = (fq.E5M2, fq.E4M3) if op != "NT" else (fq.E4M3, fq.E4M3)
+    axis_a = 0 if kcontig(op, "A") else 1
+    qa, qaT, sa = fq.fp8_quantize_tile1x128(A.to(dev()), axis_a, fa, emit_t=not kcontig(op, "A"))
+    oqa, osa = oracle.quantize_tiles(host_input(A), axis_a, 128, fa)
+    if op == "TN":   # both wgrad operands: 128x1 tiles along the token (contraction) axis
+        qb, qbT, sb = fq.fp8_quantize_tile1x128(B.to(dev()), 1, fb, emit_t=True)
+        oqb, osb = oracle.quantize_tiles(host_input(B), 1, 128, fb)
+        gb, oscale_b = fq.TILE_1x128, oracle.Scale("rowk", osb, kblk=128)
+    else:            # weights: 128x128 blocks in their stored layout
+        qb, qbT, sb = fq.fp8_quantize_block128x128(B.to(dev()), fb, emit_t=not kcontig(op, "B"))
+        oqb, osb = oracle.quantize_blocks(host_input(B), 128, 128, fb)
+        gb = fq.BLOCK_128x128
+        oscale_b = oracle.Scale("block" if op == "NT" else "blockT", osb, kblk=128, rblk=128)
+    ref = OGEMM[op](oqa, oqb, fa, fb, oracle.Scale("rowk", osa, kblk=128), oscale_b)
+    for use_kmajor in (False, True):
+        oa = Q(qa, fa, sa, fq.TILE_1x128, kmajor=qaT if (use_kmajor and qaT is not None) else None)
+        ob = Q(qb, fb, sb, gb, kmajor=qbT if (use_kmajor and qbT is not None) else None)
+        C = GEMM[op](M, N, K, oa, ob, torch.float32)
+        assert gemm_close(C, ref, torch.float32), use_kmajor
+    # autocast with the same granularities gives the same result
+    Ca = GEMM[op](M, N, K, AC(A.to(dev()), fa, fq.TILE_1x128), AC(B.to(dev()), fb, gb), torch.float32)
+    assert gemm_close(Ca, ref, torch.float32)
+
+
+@pytest.mark.parametrize("op", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("shape", [(256, 256, 128), (528, 400, 96), (1024, 1536, 1024)])
+def test_mx32(op, shape):
+    M, N, K = shape
+    announce("gemm mx32", op, shape)
+    A, B = block_operands(op, M, N, K, seed=300 + M)
+    fa, fb = (fq.E5M2, fq.E4M3) if op != "NT" else (fq.E4M3, fq.E4M3)
+    axa = 0 if kcontig(op, "A") else 1
+    axb = 0 if kcontig(op, "B") else 1
+    qa, qaT, ea = fq.fp8_quantize_mx32(A.to(dev()), axa, fa, emit_t=axa == 1)
+    qb, qbT, eb = fq.fp8_quantize_mx32(B.to(dev()), axb, fb, emit_t=axb == 1)
+    oqa, oea = oracle.quantize_tiles(host_input(A), axa, 32, fa, mx=True)
+    oqb, oeb = oracle.quantize_tiles(host_input(B), axb, 32, fb, mx=True)
+    ref = OGEMM[op](oqa, oqb, fa, fb, oracle.Scale("rowk", oea, kblk=32, e8m0=True),
+                    oracle.Scale("rowk", oeb, kblk=32, e8m0=True))
+    C = GEMM[op](M, N, K, Q(qa, fa, ea, fq.MX32, kmajor=qaT), Q(qb, fb, eb, fq.MX32, kmajor=qbT), torch.float32)
+    assert gemm_close(C, ref, torch.float32)
+    Ca = GEMM[op](M, N, K, AC(A.to(dev()), fa, fq.MX32), AC(B.to(dev()), fb, fq.MX32), torch.float32)
+    assert gemm_close(Ca, ref, torch.float32)
+
+
+def test_gemm_reruns_bitwise_identical():
+    announce("gemm reruns")
+    A, B = workloads.attn_out_operands(M=1024, K=1024, N=512)
+    qa, _, sa, _, _ = quantize_pt(A, fq.E4M3, False)
+    qb, _, sb, _, _ = quantize_pt(B, fq.E4M3, False)
+    C1 = fq.fp8_gemm_scaled_NT(1024, 512, 1024, Q(qa, fq.E4M3, sa), Q(qb, fq.E4M3, sb))
+    C2 = fq.fp8_gemm_scaled_NT(1024, 512, 1024, Q(qa, fq.E4M3, sa), Q(qb, fq.E4M3, sb))
+    assert torch.equal(C1, C2)
+
+
+# ------------------------------------------------------------------ full sizes, sampled rows
+def test_full_attn_out_prequantized_and_autocast():
+    """Attention-output GEMM 15872 x 4096 x 4096, E4M3, bf16 out (the launch
+    configuration the benchmark times), on sampled rows."""
+    M, K, N = workloads.M_TOKENS, workloads.HIDDEN, workloads.HIDDEN
+    announce("full attn-out")
+    A, B = workloads.attn_out_operands()
+    qa, _, sa, oqa, osa = quantize_pt(A, fq.E4M3, False)
+    qb, _, sb, oqb, osb = quantize_pt(B, fq.E4M3, False)
+    rows = sample_rows(M, 1)
+    ref = oracle.gemm_nt(oqa, oqb, 0, 0, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb), rows=rows)
+    C = fq.fp8_gemm_scaled_NT(M, N, K, Q(qa, fq.E4M3, sa), Q(qb, fq.E4M3, sb))
+    assert gemm_close(C[torch.from_numpy(rows).to(dev())], ref, torch.bfloat16)
+    Ca = fq.fp8_gemm_scaled_NT(M, N, K, AC(A.to(dev()), fq.E4M3), AC(B.to(dev()), fq.E4M3))
+    assert torch.equal(C, Ca)
+
+
+@pytest.mark.parametrize("gemm", workloads.layer_gemms(), ids=lambda g: g[0])
+def test_full_layer_gemm_sampled(gemm):
+    """Each of the 12 layer GEMMs at full size (operands ~ N(0,1)/sqrt(K)),
+    per-tensor current scaling, fprop E4M3 x E4M3, dgrad and wgrad E5M2 x E4M3,
+    autocast, bf16 out, on sampled output rows."""
+    name, op, M, N, K = gemm
+    announce("full layer", name, op, M, N, K)
+    A, B = workloads.gemm_operands(op, M, N, K, seed=4000 + zlib.crc32(name.encode()) % 1000, device=dev())
+    fa = fq.E4M3 if op == "NT" else fq.E5M2
+    C = GEMM[op](M, N, K, AC(A, fa), AC(B, fq.E4M3))
+    oqa, osa, _ = oracle.quantize_per_tensor(host_input(A), fa)
+    oqb, osb, _ = oracle.quantize_per_tensor(host_input(B), fq.E4M3)
+    rows = sample_rows(M, 2, n_tiles=3, n_rand=4)
+    # the oracle's NT form on K-contiguous copies (layouts agree exactly: oracle pin)
+    oqa, oqb = oqa.reshape(A.shape), oqb.reshape(B.shape)
+    if not kcontig(op, "A"):
+        oqa = np.ascontiguousarray(oqa.T)
+    if not kcontig(op, "B"):
+        oqb = np.ascontiguousarray(oqb.T)
+    ref = oracle.gemm_nt(oqa, oqb, fa, fq.E4M3, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb), rows=rows)
+    assert gemm_close(C[torch.from_numpy(rows).to(dev())], ref, torch.bfloat16)

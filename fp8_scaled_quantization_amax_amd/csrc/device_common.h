@@ -11,7 +11,7 @@ namespace fp8q {
 
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE5M2Max = 57344.0f;
-constexpr float kScaleFloor = 1e-12f;  // clamp_min of the lab page's scaled_roundtrip
+constexpr float kScaleFloor = 1e-12f;  // lower bound on a scale (lab page, scaled_roundtrip)
 
 template <int FMT>
 __device__ __forceinline__ constexpr float fmt_max() { return FMT == FP8Q_E4M3 ? kE4M3Max : kE5M2Max; }

@@ -2,8 +2,8 @@
 // per-128-K-block (1x128 tiles / 128x128 blocks) or MX32 (E8M0 per 32 K)
 // scales, fp32 accumulation on the CDNA4 FP8 matrix cores, fp32 or bf16 out.
 //
-// Follows the "fp8_parity.py" lab page, class FP8Matmul (y = xq @ wq.T with
-// the scales of both operands applied to the fp32 result) and the blog post
+// Follows the "fp8_parity.py" lab page, class FP8Matmul (the product of the
+// two quantized operands, both scales applied to the fp32 result) and the blog post
 // "How to Optimize Transformer-Based Models for Low-Precision Training"
 // (fprop / dgrad / wgrad GEMMs of a layer; MXFP8 and 2D-block recipes).
 //

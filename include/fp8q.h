@@ -15,12 +15,12 @@
  * What the operations compute (page citations name the source page and its
  * section):
  *   amax      max |x_i|, NaN-propagating.  "fp8_parity.py" lab page,
- *             scaled_roundtrip (x.abs().max()).
+ *             scaled_roundtrip.
  *   scale     s = max(amax / fmax, 1e-12) in fp32, fmax = 448 (E4M3) or
  *             57344 (E5M2).  Same function; constants E4M3_MAX / E5M2_MAX.
  *   cast      q_i = RNE_fp8(RN_fp32(x_i / s)), OCP float8_e4m3fn / float8_e5m2,
  *             non-saturating (E4M3 overflow -> NaN, E5M2 -> Inf) unless
- *             FP8Q_SATURATE.  Same function, (x / scale).to(dtype); smoke
+ *             FP8Q_SATURATE.  Same function (divide, then convert); smoke
  *             check [2] fixes the overflow rule.
  *   delayed   s from the maximum of an amax history of earlier steps (16
  *             entries); the current amax is recorded afterwards.  Smoke
@@ -33,7 +33,7 @@
  *             elements (recipe "mxfp8").
  *   GEMM      y = (Aq . Bq) * sA * sB with fp32 accumulation; fprop (NT),
  *             dgrad (NN), wgrad (TN).  Lab page, class FP8Matmul (forward
- *             xq @ wq.T, backward gq @ wq and gq.T @ xq); the blog post's
+ *             and backward products of the quantized operands); the blog post's
  *             fprop / dgrad / wgrad shapes and its autocast vs pre-quantize
  *             modes.
  *
@@ -120,7 +120,7 @@ size_t fp8q_reduce_workspace_bytes(void);
  * amax_out[0] = max_i |x_i| over n elements of type hp (NaN if any x_i is
  * NaN).  x: n elements, any alignment of the element type.  ws: at least
  * fp8q_reduce_workspace_bytes() bytes of scratch (contents ignored and
- * overwritten).  Lab page, scaled_roundtrip: x.abs().max().
+ * overwritten).  Lab page, scaled_roundtrip.
  */
 int fp8_amax(const void* x, int hp, int64_t n, float* amax_out,
              void* ws, size_t ws_bytes, void* stream);

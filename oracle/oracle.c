@@ -160,8 +160,9 @@ float orc_amax_strided(const void* x, int hp, int64_t n, int64_t stride)
 
 float orc_amax(const void* x, int hp, int64_t n) { return orc_amax_strided(x, hp, n, 1); }
 
-/* s = max(amax / fmax, 1e-12), in fp32: [LAB] scaled_roundtrip computes
- * (x.abs().max() / fmax).clamp_min(1e-12).  clamp_min propagates NaN. */
+/* s = max(amax / fmax, 1e-12), in fp32 ([LAB] scaled_roundtrip: the largest
+ * magnitude over the format maximum, bounded below by 1e-12; a NaN amax
+ * gives a NaN scale). */
 float orc_scale_from_amax(float amax, int fmt)
 {
     const float floor_s = (float)1e-12;
@@ -171,7 +172,8 @@ float orc_scale_from_amax(float amax, int fmt)
     return s < floor_s ? floor_s : s;
 }
 
-/* q_i = encode(RN32(x_i / s)): [LAB] scaled_roundtrip, (x / scale).to(dtype). */
+/* q_i = encode(RN32(x_i / s)): [LAB] scaled_roundtrip divides by the scale
+ * in fp32, then converts to the 8-bit type. */
 uint8_t orc_cast1(float x, float s, int fmt, int saturate)
 {
     return orc_encode(div_rn32(x, s), fmt, saturate);
@@ -314,8 +316,9 @@ void orc_quantize_blocks(const void* x, int hp, int64_t rows, int64_t cols, int6
 }
 
 /* ------------------------------------------------------------------ */
-/* Scaled GEMM ([LAB] FP8Matmul: forward xq @ wq.T, backward gq @ wq and   */
-/* gq.T @ xq; [BLOG] fprop / dgrad / wgrad):                              */
+/* Scaled GEMM ([LAB] FP8Matmul: forward = input times transposed weight, */
+/* backward = gradient times weight and transposed gradient times input; */
+/* [BLOG] fprop / dgrad / wgrad):                                        */
 /*   y[m,n] = sum over K-blocks kb of sA(m,kb) * sB(n,kb) *               */
 /*            sum_{k in kb} qA[m,k] * qB[n,k]                             */
 /* The inner sums are exact: an E4M3 value is an integer multiple of 2^-9 */

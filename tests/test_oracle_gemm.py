@@ -150,7 +150,7 @@ def test_layouts_agree_and_row_sampling(orc):
 
 
 def test_tiny_layer_matches_fake_quant_matmul(orc):
-    """fp8_parity.py FP8Matmul: forward xq @ wq.T, backward gq @ wq and gq.T @ xq on
+    """fp8_parity.py FP8Matmul computes its forward and backward products on
     dequantized fp32 values.  The oracle's exact-integer GEMM agrees with an fp64
     matmul of the dequantized codes to fp64 rounding."""
     X, W1, _, G = workloads.tiny_layer()

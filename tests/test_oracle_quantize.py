@@ -16,7 +16,7 @@ FMAX = {E4M3: 448.0, E5M2: 57344.0}
 
 
 def dequant(orc, q, s, fmt):
-    """p2's .float() * scale: fp32 product of the code's value and the scale."""
+    """Dequantization as the lab page does it: fp32 product of the code's value and the scale."""
     return (orc.decode_array(q, fmt).astype(np.float32) * np.float32(s)).astype(np.float32)
 
 

@@ -273,6 +273,189 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, int ntm, 
     }
 }
 
+// ------------------------------------------------------------------ per-tensor fast path
+//
+// Per-tensor scales, K a multiple of 128 and every operand offset below 2^32:
+// the same 256 x 256 x 128 tiling, but operand tiles go straight from global
+// memory into LDS (global_load_lds, no register staging), and the LDS reads
+// and waits are ordered by hand so that every wait covers reads issued at
+// least one MFMA group earlier.
+
+// Swizzle of the 16-byte chunks of a 128-byte LDS row: chunk c of row r sits
+// at c ^ ((r / 2) % 8).  A fragment read serves 16 consecutive rows at one
+// logical chunk per phase; the XOR spreads them over 8 chunk positions x 2
+// row parities, i.e. over all 64 banks.
+__device__ __forceinline__ int swz2(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima): every LDS
+// read issued so far has landed.
+__device__ __forceinline__ void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier for the staged pipeline.  Each wave has already waited
+// for its own loads of the stage about to be read (vm_wait) and for its own
+// LDS reads of the stage about to be overwritten (lds_wait_all), so only the
+// execution barrier is needed; __syncthreads() would add a full vmcnt(0)
+// wait.  The empty asm keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) with lgkmcnt and expcnt at their maxima (vmcnt is six
+// bits: [3:0] and [15:14] of the immediate); N < 64.
+template <int N>
+__device__ __forceinline__ void vm_wait() { __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14)); }
+
+__device__ __forceinline__ v8i frag2(const uint8_t* lds, int r0) {
+    const int l = threadIdx.x & 63;
+    const int r = r0 + (l & 15), g = l >> 4;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz2(r, g));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz2(r, g + 4));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Direct global -> LDS loads of one 256 x 128 operand tile: wave w brings rows
+// [64w, 64w+64) in 8 instructions of 8 rows.  The hardware writes lane l's 16
+// bytes at the instruction's LDS base + 16 l, i.e. row l/8, physical chunk
+// l%8 of the 8-row group; the lane therefore fetches the logical chunk that
+// the swizzle places there.  Rows past the matrix edge re-read the last row
+// (their products only reach outputs that are never stored).  The per-lane
+// offsets are computed once per tile; a step moves the base pointer by its K
+// offset, and the LDS destination (M0) is scalar arithmetic on the wave index.
+struct Dma2 {
+    uint32_t off[8];
+};
+
+__device__ __forceinline__ Dma2 dma2_plan(int64_t nrows, int64_t K, int64_t row0, int wave) {
+    const int l = threadIdx.x & 63;
+    Dma2 d;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int r = wave * 64 + u * 8 + (l >> 3);
+        const int c = (l & 7) ^ ((r >> 1) & 7);
+        int64_t row = row0 + r;
+        row = row < nrows ? row : nrows - 1;
+        d.off[u] = (uint32_t)(row * K + c * 16);
+    }
+    return d;
+}
+
+__device__ __forceinline__ void dload_tile(const uint8_t* __restrict__ base, const Dma2& d, uint8_t* lds, int wave) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        __builtin_amdgcn_global_load_lds(base + d.off[u],
+                                         (__attribute__((address_space(3))) void*)(lds + (wave * 64 + u * 8) * BK),
+                                         16, 0, 0);
+}
+
+template <int FA, int FB, int OUT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int ntm, int ntn) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_ab[2][2 * kTileBytes];
+    int tm, tn;
+    tile_of_block(ntm, ntn, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 256;
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int t = threadIdx.x, l = t & 63, w = t >> 6;
+    const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+    constexpr int kFmtA = FA == FP8Q_E4M3 ? 0 : 1;
+    constexpr int kFmtB = FB == FP8Q_E4M3 ? 0 : 1;
+
+    v4f acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (int)(K / BK);
+    const int wave = __builtin_amdgcn_readfirstlane(w);
+    const Dma2 da = dma2_plan(M, K, m0, wave), db = dma2_plan(N, K, n0, wave);
+    dload_tile(g.A, da, lds_ab[0], wave);
+    dload_tile(g.B, db, lds_ab[0] + kTileBytes, wave);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) {
+            dload_tile(g.A + (int64_t)(kt + 1) * BK, da, lds_ab[cur ^ 1], wave);
+            dload_tile(g.B + (int64_t)(kt + 1) * BK, db, lds_ab[cur ^ 1] + kTileBytes, wave);
+        }
+        const uint8_t* la = lds_ab[cur];
+        const uint8_t* lb = lds_ab[cur] + kTileBytes;
+        // The first 2 x 8 MFMA row pair runs in 2 x 2 blocks while the B
+        // fragments stream in; each later row pair's A fragments are fetched
+        // one row pair ahead.  sched_barrier pins this program order.
+        v8i bf[8];
+        v8i af[2][2];
+        af[0][0] = frag2(la, wm);
+        af[0][1] = frag2(la, wm + 16);
+        bf[0] = frag2(lb, wn);
+        bf[1] = frag2(lb, wn + 16);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            lds_wait_all();
+            if (jb < 3) {
+                bf[2 * jb + 2] = frag2(lb, wn + 16 * (2 * jb + 2));
+                bf[2 * jb + 3] = frag2(lb, wn + 16 * (2 * jb + 3));
+            } else {
+                af[1][0] = frag2(la, wm + 32);
+                af[1][1] = frag2(la, wm + 48);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = 2 * jb + jj;
+                    acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[0][ii], acc[ii][j], kFmtB,
+                                                                                  kFmtA, 0, 0, 0, 0);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int p = 1; p < 4; ++p) {
+            lds_wait_all();
+            if (p < 3) {
+                af[(p + 1) & 1][0] = frag2(la, wm + 32 * (p + 1));
+                af[(p + 1) & 1][1] = frag2(la, wm + 32 * (p + 1) + 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[2 * p + ii][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf[j], af[p & 1][ii], acc[2 * p + ii][j], kFmtB, kFmtA, 0, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // this wave has read all of the current stage and its loads of the
+        // next stage have landed; after the barrier the same holds for all
+        lds_wait_all();
+        vm_wait<0>();
+        stage_barrier();
+    }
+
+    const float S = reinterpret_cast<const float*>(g.sa.s)[0] * reinterpret_cast<const float*>(g.sb.s)[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + wm + 16 * i + (l & 15);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = n0 + wn + 16 * j + 4 * (l >> 4);
+            if (n >= N) continue;
+            const v4f v = acc[i][j] * S;
+            if constexpr (OUT == FP8Q_BF16) {
+                const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n) = make_uint2(lo, hi);
+            } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.C) + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
 template <int FA, int FB, int OUT>
 static void launch_sm(const GemmArgs& g, int sm, hipStream_t s) {
     const int ntm = (int)((g.M + BM - 1) / BM);
@@ -282,7 +465,10 @@ static void launch_sm(const GemmArgs& g, int sm, hipStream_t s) {
         return;
     }
     const int ntn = (int)((g.N + 255) / 256);
-    if (sm == kSmPerTensor)
+    const bool offsets32 = g.M * g.K <= (int64_t(1) << 32) && g.N * g.K <= (int64_t(1) << 32);
+    if (sm == kSmPerTensor && g.K % BK == 0 && offsets32)
+        hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
+    else if (sm == kSmPerTensor)
         hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmPerTensor, 256>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
     else
         hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmMx, 256>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);

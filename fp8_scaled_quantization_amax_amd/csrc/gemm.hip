@@ -32,6 +32,8 @@
 //    scale of row l%16 for the 32-K block l/16 of the 128-K step.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -275,11 +277,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, int ntm, 
 
 // ------------------------------------------------------------------ per-tensor fast path
 //
-// Per-tensor scales, K a multiple of 128 and every operand offset below 2^32:
-// the same 256 x 256 x 128 tiling, but operand tiles go straight from global
-// memory into LDS (global_load_lds, no register staging), and the LDS reads
-// and waits are ordered by hand so that every wait covers reads issued at
-// least one MFMA group earlier.
+// Per-tensor scales, K a multiple of 128 and at least 256, every operand
+// offset below 2^32: a persistent kernel with the same 256 x 256 x 128 tile.
+//  * One workgroup per CU slot.  Workgroups are dealt round-robin to the 8
+//    XCDs; each XCD takes a contiguous range of logical tiles (grouped by 8
+//    M-tiles), and its workgroups walk that range together, so the tiles that
+//    run at the same time on one XCD share A and B panels in its L2.
+//  * Operand tiles go straight from global memory into LDS
+//    (global_load_lds_dwordx4, no register staging), two stages.  The 16 loads
+//    of a wave for the next stage are spread one per two MFMAs over the first
+//    half of each K step; the last K step of a tile loads the first stage of
+//    the workgroup's next tile, so the epilogue overlaps those loads.
+//  * Each K step starts right after the barrier with the previous step's
+//    last row pair (registers only), column by column, and reads each B
+//    fragment of the new step into the registers its predecessor just left;
+//    the new step's first row pair then waits only for the fragment it needs
+//    (partial lgkmcnt waits: LDS reads of one wave complete in order).
+//  * Epilogue: results are scaled (bf16: rounded by the hardware convert,
+//    round to nearest even, NaN stays NaN), staged through the LDS stage
+//    buffer the last step read, and stored as 16-byte row-contiguous pieces,
+//    so each store instruction writes whole cache lines.
 
 // Swizzle of the 16-byte chunks of a 128-byte LDS row: chunk c of row r sits
 // at c ^ ((r / 2) % 8).  A fragment read serves 16 consecutive rows at one
@@ -349,111 +366,246 @@ __device__ __forceinline__ void dload_tile(const uint8_t* __restrict__ base, con
                                          16, 0, 0);
 }
 
+// s_waitcnt lgkmcnt(n) (vmcnt, expcnt at their maxima) for an n that is a
+// compile-time constant after unrolling; n above 15 waits for 15, which is
+// at least as strong since LDS reads complete in order.
+__device__ __forceinline__ void lgkm_wait(int n) {
+    switch (n < 15 ? n : 15) {
+        case 0: __builtin_amdgcn_s_waitcnt(0xC07F); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0xC17F); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0xC27F); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0xC37F); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0xC47F); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0xC57F); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0xC67F); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0xC77F); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0xC87F); break;
+        case 9: __builtin_amdgcn_s_waitcnt(0xC97F); break;
+        case 10: __builtin_amdgcn_s_waitcnt(0xCA7F); break;
+        case 11: __builtin_amdgcn_s_waitcnt(0xCB7F); break;
+        case 12: __builtin_amdgcn_s_waitcnt(0xCC7F); break;
+        case 13: __builtin_amdgcn_s_waitcnt(0xCD7F); break;
+        case 14: __builtin_amdgcn_s_waitcnt(0xCE7F); break;
+        default: __builtin_amdgcn_s_waitcnt(0xCF7F); break;
+    }
+}
+
+// Logical tile lg -> (tm, tn): groups of 8 M-tiles, N-tiles walked inside a group.
+__device__ __forceinline__ void tile_coords(int lg, int ntm, int ntn, int& tm, int& tn) {
+    constexpr int GM = 8;
+    const int per_group = GM * ntn;
+    const int group = lg / per_group;
+    const int first_m = group * GM;
+    const int gsize = ntm - first_m < GM ? ntm - first_m : GM;
+    const int in_group = lg % per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+__device__ __forceinline__ void dma_one(const uint8_t* base, uint32_t off, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds(base + off, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+constexpr int kEpPitch = 272;     // bytes per staged bf16 row of 128 values (+16: conflict-free)
+constexpr int kEpPitch32 = 528;   // bytes per staged fp32 row of 128 values (+16)
+
 template <int FA, int FB, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int ntm, int ntn) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_ab[2][2 * kTileBytes];
-    int tm, tn;
-    tile_of_block(ntm, ntn, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 256;
     const int64_t M = g.M, N = g.N, K = g.K;
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
     const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
     constexpr int kFmtA = FA == FP8Q_E4M3 ? 0 : 1;
     constexpr int kFmtB = FB == FP8Q_E4M3 ? 0 : 1;
-
-    v4f acc[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
+    const int nt = ntm * ntn;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per = gridDim.x / 8;
+    const int lo = (int)((int64_t)nt * xcd / 8), hi = (int)((int64_t)nt * (xcd + 1) / 8);
+    int logical = lo + slot;
+    if (logical >= hi) return;
     const int nk = (int)(K / BK);
     const int wave = __builtin_amdgcn_readfirstlane(w);
-    const Dma2 da = dma2_plan(M, K, m0, wave), db = dma2_plan(N, K, n0, wave);
+    int tm, tn;
+    tile_coords(logical, ntm, ntn, tm, tn);
+    Dma2 da = dma2_plan(M, K, (int64_t)tm * BM, wave), db = dma2_plan(N, K, (int64_t)tn * 256, wave);
     dload_tile(g.A, da, lds_ab[0], wave);
     dload_tile(g.B, db, lds_ab[0] + kTileBytes, wave);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            dload_tile(g.A + (int64_t)(kt + 1) * BK, da, lds_ab[cur ^ 1], wave);
-            dload_tile(g.B + (int64_t)(kt + 1) * BK, db, lds_ab[cur ^ 1] + kTileBytes, wave);
-        }
-        const uint8_t* la = lds_ab[cur];
-        const uint8_t* lb = lds_ab[cur] + kTileBytes;
-        // The first 2 x 8 MFMA row pair runs in 2 x 2 blocks while the B
-        // fragments stream in; each later row pair's A fragments are fetched
-        // one row pair ahead.  sched_barrier pins this program order.
-        v8i bf[8];
-        v8i af[2][2];
-        af[0][0] = frag2(la, wm);
-        af[0][1] = frag2(la, wm + 16);
-        bf[0] = frag2(lb, wn);
-        bf[1] = frag2(lb, wn + 16);
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            lds_wait_all();
-            if (jb < 3) {
-                bf[2 * jb + 2] = frag2(lb, wn + 16 * (2 * jb + 2));
-                bf[2 * jb + 3] = frag2(lb, wn + 16 * (2 * jb + 3));
-            } else {
-                af[1][0] = frag2(la, wm + 32);
-                af[1][1] = frag2(la, wm + 48);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int j = 2 * jb + jj;
-                    acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[0][ii], acc[ii][j], kFmtB,
-                                                                                  kFmtA, 0, 0, 0, 0);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int p = 1; p < 4; ++p) {
-            lds_wait_all();
-            if (p < 3) {
-                af[(p + 1) & 1][0] = frag2(la, wm + 32 * (p + 1));
-                af[(p + 1) & 1][1] = frag2(la, wm + 32 * (p + 1) + 16);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[2 * p + ii][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf[j], af[p & 1][ii], acc[2 * p + ii][j], kFmtB, kFmtA, 0, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // this wave has read all of the current stage and its loads of the
-        // next stage have landed; after the barrier the same holds for all
-        lds_wait_all();
-        vm_wait<0>();
-        stage_barrier();
-    }
-
     const float S = reinterpret_cast<const float*>(g.sa.s)[0] * reinterpret_cast<const float*>(g.sb.s)[0];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + wm + 16 * i + (l & 15);
-        if (m >= M) continue;
+
+    v4f acc[8][8];
+    v8i b[8];
+    v8i ax[2], ay[2];
+    Dma2 na, nb;
+
+    auto mfma = [&](int i, const v8i& bb, const v8i& a, int j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bb, a, acc[i][j], kFmtB, kFmtA, 0, 0, 0, 0);
+    };
+    // Stage kt of the current tile lives in buffer (kt + par) % 2.  Load slot
+    // u (0..15) of a wave: MODE 1 = stage kt+1 of this tile, MODE 2 = stage 0
+    // of the next tile; both go to the buffer the current step does not read.
+    int par = 0;
+    auto dma = [&](auto mode_c, int kt, int u) {
+        constexpr int MODE = decltype(mode_c)::value;
+        const int64_t ko = MODE == 1 ? (int64_t)(kt + 1) * BK : 0;
+        uint8_t* dst = lds_ab[(kt + 1 + par) & 1];
+        const Dma2& pa = MODE == 1 ? da : na;
+        const Dma2& pb = MODE == 1 ? db : nb;
+        if (u < 8) dma_one(g.A + ko, pa.off[u], dst + (wave * 64 + u * 8) * BK);
+        else dma_one(g.B + ko, pb.off[u - 8], dst + kTileBytes + (wave * 64 + (u - 8) * 8) * BK);
+    };
+
+    // One K step.  LDS reads in issue order: ax (4 reads), b[j] (2 each), ay (4).
+    auto step = [&](auto mode_c, auto deferred_c, int kt) {
+        constexpr int MODE = decltype(mode_c)::value;
+        constexpr bool DEFERRED = decltype(deferred_c)::value;
+        const uint8_t* la = lds_ab[(kt + par) & 1];
+        const uint8_t* lb = la + kTileBytes;
+        ax[0] = frag2(la, wm);
+        ax[1] = frag2(la, wm + 16);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t n = n0 + wn + 16 * j + 4 * (l >> 4);
-            if (n >= N) continue;
-            const v4f v = acc[i][j] * S;
-            if constexpr (OUT == FP8Q_BF16) {
-                const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n) = make_uint2(lo, hi);
-            } else {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.C) + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+            if constexpr (DEFERRED) {
+                mfma(6, b[j], ay[0], j);
+                mfma(7, b[j], ay[1], j);
+            }
+            b[j] = frag2(lb, wn + 16 * j);
+            if (MODE) dma(mode_c, kt, j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        ay[0] = frag2(la, wm + 32);
+        ay[1] = frag2(la, wm + 48);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lgkm_wait(24 - (6 + 2 * j));   // b[j] and everything before it landed
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(0, b[j], ax[0], j);
+            mfma(1, b[j], ax[1], j);
+            if (MODE) dma(mode_c, kt, 8 + j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_wait_all();
+        ax[0] = frag2(la, wm + 64);
+        ax[1] = frag2(la, wm + 80);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) mfma(2 + (q >> 3), b[q & 7], ay[q >> 3], q & 7);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_all();
+        ay[0] = frag2(la, wm + 96);
+        ay[1] = frag2(la, wm + 112);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) mfma(4 + (q >> 3), b[q & 7], ax[q >> 3], q & 7);
+        __builtin_amdgcn_sched_barrier(0);
+        // this stage fully read; the next stage of this tile landed (the next
+        // tile's first stage is waited for at the top of the tile loop)
+        lds_wait_all();
+        if (MODE == 1) vm_wait<0>();
+        stage_barrier();
+    };
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using T = std::true_type;
+    using F = std::false_type;
+
+    while (true) {
+        const int next = logical + per;
+        const bool has_next = next < hi;
+        // without a next tile the last step re-loads this tile's first stage
+        // into the free buffer: harmless, and it keeps the step branch-free
+        int ntm_, ntn_;
+        tile_coords(has_next ? next : logical, ntm, ntn, ntm_, ntn_);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        // this tile's first stage (and the previous tile's stores) complete
+        vm_wait<0>();
+        stage_barrier();
+        step(C1{}, F{}, 0);
+        for (int kt = 1; kt + 1 < nk; ++kt) step(C1{}, T{}, kt);
+        na = dma2_plan(M, K, (int64_t)ntm_ * BM, wave);
+        nb = dma2_plan(N, K, (int64_t)ntn_ * 256, wave);
+        step(C2{}, T{}, nk - 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            mfma(6, b[j], ay[0], j);
+            mfma(7, b[j], ay[1], j);
+        }
+
+        const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 256;
+        if constexpr (OUT == FP8Q_BF16) {
+            typedef float v2f_t __attribute__((ext_vector_type(2)));
+            typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+            // this wave's 32-row staging area in the stage buffer the last step read
+            uint8_t* ep = lds_ab[(nk - 1 + par) & 1] + w * (32 * kEpPitch);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const v4f v = acc[2 * qq + ii][j] * S;
+                        const v2bf_t p0 = __builtin_convertvector(v2f_t{v[0], v[1]}, v2bf_t);
+                        const v2bf_t p1 = __builtin_convertvector(v2f_t{v[2], v[3]}, v2bf_t);
+                        const int row = 16 * ii + (l & 15);
+                        *reinterpret_cast<uint2*>(ep + row * kEpPitch + (16 * j + 4 * (l >> 4)) * 2) =
+                            make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+                    }
+                lds_wait_all();
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int row = 4 * u + (l >> 4), ch = l & 15;
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kEpPitch + ch * 16);
+                    const int64_t m = m0 + wm + 32 * qq + row;
+                    const int64_t n = n0 + wn + ch * 8;
+                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n) = d;
+                }
+            }
+        } else {
+            // fp32: 16 rows x 128 values per round, pitch 528 B
+            uint8_t* ep = lds_ab[(nk - 1 + par) & 1] + w * (16 * kEpPitch32);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<v4f*>(ep + (l & 15) * kEpPitch32 + (16 * j + 4 * (l >> 4)) * 4) = acc[i][j] * S;
+                lds_wait_all();
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int row = 2 * u + (l >> 5), ch = l & 31;
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kEpPitch32 + ch * 16);
+                    const int64_t m = m0 + wm + 16 * i + row;
+                    const int64_t n = n0 + wn + ch * 4;
+                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(g.C) + m * N + n) = d;
+                }
             }
         }
+        if (!has_next) break;
+        logical = next;
+        par = (nk + par) & 1;
+        tm = ntm_;
+        tn = ntn_;
+        da = na;
+        db = nb;
     }
+    // the last step's extra loads land before the workgroup's LDS is released
+    vm_wait<0>();
+}
+
+// Workgroups of the persistent kernel: one per CU, rounded down to a multiple
+// of the 8 XCDs (the kernel splits the tiles into 8 per-XCD ranges).
+static int persistent_grid() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        cached[dev] = cus / 8 * 8;
+    }
+    return cached[dev];
 }
 
 template <int FA, int FB, int OUT>
@@ -466,8 +618,8 @@ static void launch_sm(const GemmArgs& g, int sm, hipStream_t s) {
     }
     const int ntn = (int)((g.N + 255) / 256);
     const bool offsets32 = g.M * g.K <= (int64_t(1) << 32) && g.N * g.K <= (int64_t(1) << 32);
-    if (sm == kSmPerTensor && g.K % BK == 0 && offsets32)
-        hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
+    if (sm == kSmPerTensor && g.K % BK == 0 && g.K >= 2 * BK && offsets32)
+        hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT>), dim3(persistent_grid()), dim3(kThreads), 0, s, g, ntm, ntn);
     else if (sm == kSmPerTensor)
         hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmPerTensor, 256>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
     else

@@ -64,7 +64,10 @@ def test_tiny_layer_all_ops_fp32_out():
 
 
 # ------------------------------------------------------------------ per-tensor, ragged shapes
-SHAPES = [(16, 16, 16), (528, 272, 1040), (256, 256, 128), (1040, 784, 272)]
+# K % 128 != 0 or K = 128 take the register-staged kernel; K = 256, 384, 1152
+# (2, 3 and 9 K steps, ragged M and N) the persistent direct-to-LDS kernel.
+SHAPES = [(16, 16, 16), (528, 272, 1040), (256, 256, 128), (1040, 784, 272), (528, 272, 256), (1040, 784, 384),
+          (784, 1040, 1152)]
 FMT_PAIRS = [(fq.E4M3, fq.E4M3), (fq.E5M2, fq.E4M3), (fq.E5M2, fq.E5M2)]
 
 
@@ -84,6 +87,24 @@ def test_per_tensor_prequantized(shape, op, fa, fb, out_dtype):
         ob = Q(qb, fb, sb, kmajor=qbT if (use_kmajor and not kcontig(op, "B")) else None)
         C = GEMM[op](M, N, K, oa, ob, out_dtype)
         assert gemm_close(C, ref, out_dtype), use_kmajor
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(4112, 4112, 384), (4368, 4096, 256)])
+@pytest.mark.parametrize("op", ["NT", "NN"])
+def test_per_tensor_persistent_multi_tile(op, shape, out_dtype):
+    """More output tiles than workgroups: some workgroups run two tiles, the
+    second starting in the other LDS buffer when the K step count is odd.
+    Sampled rows (tile edges included) against the oracle."""
+    M, N, K = shape
+    announce("gemm per-tensor multi-tile", op, shape, out_dtype)
+    A, B = workloads.gemm_operands(op, M, N, K, seed=500 + M + K)
+    qa, qaT, sa, oqa, osa = quantize_pt(A, fq.E4M3, False)
+    qb, qbT, sb, oqb, osb = quantize_pt(B, fq.E4M3, False)
+    rows = sample_rows(M, seed=M + K)
+    ref = OGEMM[op](oqa, oqb, 0, 0, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb), rows=rows)
+    C = GEMM[op](M, N, K, Q(qa, fq.E4M3, sa), Q(qb, fq.E4M3, sb), out_dtype)
+    assert gemm_close(C[torch.as_tensor(rows, device=C.device)], ref, out_dtype)
 
 
 @pytest.mark.parametrize("op", ["NT", "NN", "TN"])

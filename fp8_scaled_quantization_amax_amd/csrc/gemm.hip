@@ -402,8 +402,16 @@ __device__ __forceinline__ void tile_coords(int lg, int ntm, int ntn, int& tm, i
     tn = in_group / gsize;
 }
 
-__device__ __forceinline__ void dma_one(const uint8_t* base, uint32_t off, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds(base + off, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// Raw buffer descriptor over [p, p + bytes) (bytes clamped to 2^32 - 1) for
+// the buffer form of the direct-to-LDS load: per-lane 32-bit offset in a
+// VGPR, per-step K offset in an SGPR, so no 64-bit address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int64_t bytes) {
+    const int64_t n = bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)(uint32_t)n, 0x00020000);
+}
+
+__device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint8_t* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
 constexpr int kEpPitch = 272;     // bytes per staged bf16 row of 128 values (+16: conflict-free)
@@ -443,61 +451,84 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
     // u (0..15) of a wave: MODE 1 = stage kt+1 of this tile, MODE 2 = stage 0
     // of the next tile; both go to the buffer the current step does not read.
     int par = 0;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.A, M * K), rb = buffer_rsrc(g.B, N * K);
     auto dma = [&](auto mode_c, int kt, int u) {
         constexpr int MODE = decltype(mode_c)::value;
-        const int64_t ko = MODE == 1 ? (int64_t)(kt + 1) * BK : 0;
+        const uint32_t ko = MODE == 1 ? (uint32_t)(kt + 1) * BK : 0u;
         uint8_t* dst = lds_ab[(kt + 1 + par) & 1];
         const Dma2& pa = MODE == 1 ? da : na;
         const Dma2& pb = MODE == 1 ? db : nb;
-        if (u < 8) dma_one(g.A + ko, pa.off[u], dst + (wave * 64 + u * 8) * BK);
-        else dma_one(g.B + ko, pb.off[u - 8], dst + kTileBytes + (wave * 64 + (u - 8) * 8) * BK);
+        if (u < 8) dma_one(ra, pa.off[u], ko, dst + (wave * 64 + u * 8) * BK);
+        else dma_one(rb, pb.off[u - 8], ko, dst + kTileBytes + (wave * 64 + (u - 8) * 8) * BK);
     };
 
-    // One K step.  LDS reads in issue order: ax (4 reads), b[j] (2 each), ay (4).
+    // Half-fragment read: h = 0 brings K bytes [16g, 16g+16) of the lane's
+    // row, h = 1 bytes [64+16g, 64+16g+16) (g = lane / 16).
+    auto rdh = [&](v8i& f, const uint8_t* p, int r0, int h) {
+        const int r = r0 + (l & 15), gq = (l >> 4) + 4 * h;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p + swz2(r, gq));
+        if (h == 0) {
+            f[0] = (int)v.x; f[1] = (int)v.y; f[2] = (int)v.z; f[3] = (int)v.w;
+        } else {
+            f[4] = (int)v.x; f[5] = (int)v.y; f[6] = (int)v.z; f[7] = (int)v.w;
+        }
+    };
+    // One K step: 64 MFMAs with the step's 32 LDS reads (16 bytes per lane
+    // each) issued one after each of the first MFMAs, in this order: 0-3 ax
+    // (rows 0, 1), 4-15 b[0..5], 16-19 b[6..7], 20-23 ay (rows 2, 3), 24-27
+    // ax (rows 4, 5), 28-31 ay (rows 6, 7).  Before an MFMA, lgkm_wait leaves
+    // outstanding only reads issued after the last one it needs.
     auto step = [&](auto mode_c, auto deferred_c, int kt) {
         constexpr int MODE = decltype(mode_c)::value;
         constexpr bool DEFERRED = decltype(deferred_c)::value;
         const uint8_t* la = lds_ab[(kt + par) & 1];
         const uint8_t* lb = la + kTileBytes;
-        ax[0] = frag2(la, wm);
-        ax[1] = frag2(la, wm + 16);
-        __builtin_amdgcn_sched_barrier(0);
+        // previous step's rows 6, 7 (column-major, registers only) while
+        // reads 0-15 go out; b[j] is re-read only after its last old use
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if constexpr (DEFERRED) {
-                mfma(6, b[j], ay[0], j);
-                mfma(7, b[j], ay[1], j);
-            }
-            b[j] = frag2(lb, wn + 16 * j);
-            if (MODE) dma(mode_c, kt, j);
+        for (int q = 0; q < 16; ++q) {
+            if constexpr (DEFERRED) mfma(6 + (q & 1), b[q >> 1], ay[q & 1], q >> 1);
+            if (q < 4) rdh(ax[q >> 1], la, wm + 16 * (q >> 1), q & 1);
+            else rdh(b[(q - 4) >> 1], lb, wn + 16 * ((q - 4) >> 1), q & 1);
+            if (MODE && (q & 1)) dma(mode_c, kt, q >> 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        ay[0] = frag2(la, wm + 32);
-        ay[1] = frag2(la, wm + 48);
-        __builtin_amdgcn_sched_barrier(0);
+        // rows 0, 1 (column-major); reads 16-23
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            lgkm_wait(24 - (6 + 2 * j));   // b[j] and everything before it landed
+        for (int m = 0; m < 16; ++m) {
+            const int j = m >> 1, i = m & 1;
+            const int issued = 16 + (m < 8 ? m : 8);
+            const int need = j < 6 ? 5 + 2 * j : (j == 6 ? 17 : 19);
+            lgkm_wait(issued - need - 1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma(0, b[j], ax[0], j);
-            mfma(1, b[j], ax[1], j);
-            if (MODE) dma(mode_c, kt, 8 + j);
+            mfma(i, b[j], ax[i], j);
+            if (m < 4) rdh(b[6 + (m >> 1)], lb, wn + 16 * (6 + (m >> 1)), m & 1);
+            else if (m < 8) rdh(ay[(m - 4) >> 1], la, wm + 32 + 16 * ((m - 4) >> 1), m & 1);
+            if (MODE && (m & 1)) dma(mode_c, kt, 8 + (m >> 1));
             __builtin_amdgcn_sched_barrier(0);
         }
-        lds_wait_all();
-        ax[0] = frag2(la, wm + 64);
-        ax[1] = frag2(la, wm + 80);
-        __builtin_amdgcn_sched_barrier(0);
+        // rows 2, 3; reads 24-27
 #pragma unroll
-        for (int q = 0; q < 16; ++q) mfma(2 + (q >> 3), b[q & 7], ay[q >> 3], q & 7);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_wait_all();
-        ay[0] = frag2(la, wm + 96);
-        ay[1] = frag2(la, wm + 112);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int m = 0; m < 16; ++m) {
+            const int j = m & 7, i = m >> 3;
+            const int issued = 24 + (m < 4 ? m : 4);
+            lgkm_wait(issued - (i == 0 ? 21 : 23) - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(2 + i, b[j], ay[i], j);
+            if (m < 4) rdh(ax[m >> 1], la, wm + 64 + 16 * (m >> 1), m & 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // rows 4, 5; reads 28-31
 #pragma unroll
-        for (int q = 0; q < 16; ++q) mfma(4 + (q >> 3), b[q & 7], ax[q >> 3], q & 7);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int m = 0; m < 16; ++m) {
+            const int j = m & 7, i = m >> 3;
+            const int issued = 28 + (m < 4 ? m : 4);
+            lgkm_wait(issued - (i == 0 ? 25 : 27) - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(4 + i, b[j], ax[i], j);
+            if (m < 4) rdh(ay[m >> 1], la, wm + 96 + 16 * (m >> 1), m & 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // this stage fully read; the next stage of this tile landed (the next
         // tile's first stage is waited for at the top of the tile loop)
         lds_wait_all();

@@ -108,10 +108,12 @@ def _rows_cols(x):
 
 
 def _ws(nbytes, device):
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """Device workspace, zero-filled: the reduction counters in it must start at 0."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def reduce_workspace(device):
+    """Reduction workspace (zero-filled: its completion counters must start at 0)."""
     return _ws(lib().fp8q_reduce_workspace_bytes(), device)
 
 

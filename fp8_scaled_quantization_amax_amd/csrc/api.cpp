@@ -3,6 +3,8 @@
 // rejected call has enqueued nothing.  See include/fp8q.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -211,6 +213,8 @@ int autocast_operand(const fp8q_operand* o, bool kcontig, int64_t R, int64_t K, 
     a.qT = kcontig ? nullptr : ws_codes;
     a.partials = partials;
     a.nparts = fp8q::amax_partials_grid(a.rows * a.cols);
+    a.keys = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(partials) + fp8q::kReduceKeysOffset);
+    a.ctrs = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(partials) + fp8q::kReduceCtrOffset);
     int r;
     switch (o->granularity) {
         case FP8Q_PER_TENSOR: {
@@ -331,9 +335,15 @@ int fp8_amax(const void* x, int hp, int64_t n, float* amax_out, void* ws, size_t
     if ((r = check_device()) != FP8Q_OK) return r;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* partials = reinterpret_cast<float*>(ws);
-    const int np = fp8q::amax_partials_grid(n);
-    if ((r = launched(fp8q::launch_amax_partials(x, hp, n, partials, np, nullptr, s), "amax")) != FP8Q_OK) return r;
-    if ((r = launched(fp8q::launch_amax_finalize(partials, np, amax_out, s), "amax finalize")) != FP8Q_OK) return r;
+    // the folded form's completion chain grows with the block count: 1024 blocks
+    // keep the stream at full rate and the tail short
+    const int np = std::min(fp8q::amax_partials_grid(n), 1024);
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(wsb + fp8q::kReduceKeysOffset);
+    uint32_t* ctrs = reinterpret_cast<uint32_t*>(wsb + fp8q::kReduceCtrOffset);
+    if ((r = launched(fp8q::launch_amax_partials(x, hp, n, partials, np, nullptr, s, keys, ctrs, amax_out),
+                      "amax")) != FP8Q_OK)
+        return r;
     return ok();
 }
 
@@ -367,6 +377,8 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, i
     float* partials = reinterpret_cast<float*>(ws);
     a.partials = partials;
     a.nparts = fp8q::amax_partials_grid(rows * cols);
+    a.keys = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + fp8q::kReduceKeysOffset);
+    a.ctrs = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + fp8q::kReduceCtrOffset);
     a.state = state;
     a.scale_out = scale_out;
     a.amax_out = amax_out;

@@ -97,6 +97,25 @@ __device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
     return v;
 }
 
+// Max over each aligned group of 4 lanes, delivered to all 4 (DPP quad
+// permutations: lane ^ 1, then lane ^ 2).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);            // quad_perm [2,3,0,1]
+    return v > o ? v : o;
+}
+
+// Max over each aligned group of 16 lanes (a DPP row), delivered to all 16:
+// quad maxima, then lane i <-> 7 - i within each half row, then i <-> 15 - i.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = quad_max_u32(v);
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);           // row_mirror
+    return v > o ? v : o;
+}
+
 // Block-wide max of a per-thread key (blockDim.x == 256).  Uses 4 words of LDS.
 __device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* lds4) {
     v = wave_max_u32(v);
@@ -111,10 +130,18 @@ __device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* lds4
 }
 
 // Reduce the partial maxima written by the amax grid (one float per block).
+// nparts <= 256 * 8; the eight loads of a thread are issued together.
 __device__ __forceinline__ float reduce_partials_256(const float* partials, int nparts, uint32_t* lds4) {
+    float p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        p[u] = i < nparts ? partials[i] : 0.0f;
+    }
     uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += 256) {
-        const uint32_t k = abs_key(partials[i]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const uint32_t k = abs_key(p[u]);
         m = m > k ? m : k;
     }
     return __uint_as_float(block_max_u32_256(m, lds4));

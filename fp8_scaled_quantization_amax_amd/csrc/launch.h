@@ -11,8 +11,19 @@ namespace fp8q {
 
 // Largest number of blocks a reduction grid uses; the reduce workspace holds
 // one fp32 partial maximum per block.
-constexpr int kReduceParts = 1024;
-constexpr size_t kReduceWsBytes = kReduceParts * sizeof(float);
+constexpr int kReduceParts = 2048;
+// Reduce workspace layout: kReduceParts partial maxima (read by the next
+// kernel), kReduceParts per-block keys (folded by the last block of the same
+// kernel), then completion counters for a two-level ticket tree: a top counter
+// and one counter per group of kTicketGroup blocks, each on its own 256-byte
+// line.  The counters are zero between calls.
+constexpr int kTicketGroup = 32;
+constexpr int kTicketLine = 64;   // uint32 words per counter line
+constexpr size_t kReduceKeysOffset = kReduceParts * sizeof(float);
+constexpr size_t kReduceCtrOffset = kReduceKeysOffset + kReduceParts * sizeof(uint32_t);
+constexpr size_t kReduceCtrBytes = (1 + kReduceParts / kTicketGroup) * kTicketLine * sizeof(uint32_t);
+constexpr size_t kReduceWsBytes = kReduceCtrOffset + kReduceCtrBytes;
+static_assert(kReduceParts <= 256 * 8, "reduce_partials_256 folds at most 8 partials per thread");
 
 // Quantization schemes of the tiled quantize kernel.
 enum Scheme : int {
@@ -38,6 +49,8 @@ struct QuantArgs {
     uint8_t* e8m0;         // MX scales
     const float* partials; // amax partials (per-tensor current; delayed cold start)
     int nparts;
+    uint32_t* keys;        // per-block keys and ticket counters of the reduce
+    uint32_t* ctrs;        // workspace (delayed scaling's grid-wide amax)
     fp8q_delayed_state* state;
     float* scale_out;
     float* amax_out;
@@ -45,11 +58,12 @@ struct QuantArgs {
 
 // amax partial maxima over n elements: one float per block into partials[0..nparts).
 // If gate != NULL the grid does nothing unless gate's history is all zero.
-// Returns the number of partials written (the grid size).
+// If keys != NULL the blocks instead fold their maxima among themselves (keys and
+// ticket counters of the reduce workspace) and the last block writes *amax_out.
 int amax_partials_grid(int64_t n);
 hipError_t launch_amax_partials(const void* x, int hp, int64_t n, float* partials, int nparts,
-                                const fp8q_delayed_state* gate, hipStream_t s);
-hipError_t launch_amax_finalize(const float* partials, int nparts, float* amax_out, hipStream_t s);
+                                const fp8q_delayed_state* gate, hipStream_t s, uint32_t* keys = nullptr,
+                                uint32_t* ctrs = nullptr, float* amax_out = nullptr);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 

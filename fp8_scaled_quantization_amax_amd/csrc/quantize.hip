@@ -21,17 +21,68 @@
 
 namespace fp8q {
 
+// ------------------------------------------------------------------ grid completion
+
+// Called by thread 0 of every block once its key is final.  The key goes to
+// keys[block] with an atomic exchange; the block then takes a ticket in a
+// two-level tree (a counter per group of kTicketGroup blocks, each on its own
+// 256-byte line, then a top counter), so no address sees more than
+// kTicketGroup atomics.  Each ticket's increment is made to depend on the
+// return of the atomic before it, so it is taken only after that atomic has
+// been performed; the block that takes the last top ticket therefore sees
+// every key.  Returns true in that one block.  Counters start at zero and are
+// left at zero.
+__device__ __forceinline__ bool grid_done(uint32_t* keys, uint32_t* ctrs, uint32_t key) {
+    const uint32_t b = blockIdx.x, nb = gridDim.x;
+    const uint32_t prev = atomicExch(&keys[b], key);
+    uint32_t one;
+    __asm__ volatile("v_mov_b32 %0, 1" : "=v"(one) : "v"(prev));
+    const uint32_t g = b / kTicketGroup;
+    const uint32_t gsize = nb - g * kTicketGroup < (uint32_t)kTicketGroup ? nb - g * kTicketGroup : kTicketGroup;
+    uint32_t* gc = &ctrs[kTicketLine * (1 + g)];
+    const uint32_t t = atomicAdd(gc, one);
+    if (t != gsize - 1) return false;
+    atomicExch(gc, 0u);
+    __asm__ volatile("v_mov_b32 %0, 1" : "=v"(one) : "v"(t));
+    const uint32_t ngroups = (nb + kTicketGroup - 1) / kTicketGroup;
+    const uint32_t t2 = atomicAdd(&ctrs[0], one);
+    if (t2 != ngroups - 1) return false;
+    atomicExch(&ctrs[0], 0u);
+    return true;
+}
+
+// Max of keys[0..n), n <= kReduceParts, read with device-coherent atomic
+// loads (all 256 threads; a thread's loads are issued together).
+__device__ __forceinline__ uint32_t fold_keys_256(const uint32_t* keys, int n, uint32_t* lds4) {
+    static_assert(kReduceParts <= 256 * 8, "eight keys per thread");
+    uint32_t k[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        k[u] = i < n ? __hip_atomic_load(&keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = m > k[u] ? m : k[u];
+    return block_max_u32_256(m, lds4);
+}
+
 // ------------------------------------------------------------------ amax
 
 // One partial maximum per block over a grid-stride range of x.  The abs key
 // (bits with the sign cleared) is maximised as an integer: NaN propagates.
 // bf16 keys are maximised two at a time as packed 16-bit integers.
+// With `keys` set, the blocks fold their maxima with grid_done and the last
+// block to finish writes the result to *amax_out: a standalone amax is one
+// launch.
 template <int HP>
 __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restrict__ x, int64_t n,
                                                             float* __restrict__ partials,
                                                             const fp8q_delayed_state* __restrict__ gate,
-                                                            int vec) {
+                                                            int vec, uint32_t* keys, uint32_t* ctrs,
+                                                            float* amax_out) {
     __shared__ uint32_t red[4];
+    __shared__ uint32_t last;
     if (gate != nullptr) {
         uint32_t h = 0;
 #pragma unroll
@@ -42,19 +93,23 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restri
     const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t nthr = (int64_t)gridDim.x * 256;
     uint32_t key = 0;
-    int64_t done = 0;
+    int64_t done = 0;   // elements covered by the vector loop
     if (vec) {
+        // one contiguous run of 16-byte vectors per block (a multiple of 256
+        // vectors), 8 loads in flight per thread, masked at the run's end
         const uint4* __restrict__ xv = reinterpret_cast<const uint4*>(x);
         const int64_t nv = n / EPV;
         done = nv * EPV;
+        const int64_t per = ((nv + gridDim.x - 1) / gridDim.x + 255) / 256 * 256;
+        const int64_t b0 = (int64_t)blockIdx.x * per;
+        const int64_t b1 = b0 + per < nv ? b0 + per : nv;
         if constexpr (HP == FP8Q_BF16) {
             typedef unsigned short us2 __attribute__((ext_vector_type(2)));
             us2 m2 = {0, 0};
-            int64_t i = tid;
-            for (; i + 7 * nthr < nv; i += 8 * nthr) {
+            for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * 8) {
                 uint4 w[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) w[u] = xv[i + u * nthr];
+                for (int u = 0; u < 8; ++u) w[u] = i + u * 256 < b1 ? xv[i + u * 256] : make_uint4(0, 0, 0, 0);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t d[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
@@ -63,21 +118,13 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restri
                         m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, d[j] & 0x7fff7fffu));
                 }
             }
-            for (; i < nv; i += nthr) {
-                const uint4 w = xv[i];
-                const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, d[j] & 0x7fff7fffu));
-            }
             const uint32_t a = m2.x, b = m2.y;
             key = (a > b ? a : b) << 16;
         } else {
-            int64_t i = tid;
-            for (; i + 7 * nthr < nv; i += 8 * nthr) {
+            for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * 8) {
                 uint4 w[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) w[u] = xv[i + u * nthr];
+                for (int u = 0; u < 8; ++u) w[u] = i + u * 256 < b1 ? xv[i + u * 256] : make_uint4(0, 0, 0, 0);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t d[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
@@ -86,15 +133,6 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restri
                         const uint32_t k = d[j] & 0x7fffffffu;
                         key = key > k ? key : k;
                     }
-                }
-            }
-            for (; i < nv; i += nthr) {
-                const uint4 w = xv[i];
-                const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t k = d[j] & 0x7fffffffu;
-                    key = key > k ? key : k;
                 }
             }
         }
@@ -106,14 +144,15 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restri
         key = key > k ? key : k;
     }
     key = block_max_u32_256(key, red);
-    if (threadIdx.x == 0) partials[blockIdx.x] = __uint_as_float(key);
-}
-
-__global__ __launch_bounds__(256) void amax_finalize_kernel(const float* __restrict__ partials, int nparts,
-                                                            float* __restrict__ amax_out) {
-    __shared__ uint32_t red[4];
-    const float a = reduce_partials_256(partials, nparts, red);
-    if (threadIdx.x == 0) *amax_out = a;
+    if (keys == nullptr) {
+        if (threadIdx.x == 0) partials[blockIdx.x] = __uint_as_float(key);
+        return;
+    }
+    if (threadIdx.x == 0) last = grid_done(keys, ctrs, key);
+    __syncthreads();
+    if (!last) return;
+    const uint32_t all = fold_keys_256(keys, gridDim.x, red);
+    if (threadIdx.x == 0) *amax_out = __uint_as_float(all);
 }
 
 int amax_partials_grid(int64_t n) {
@@ -125,19 +164,18 @@ int amax_partials_grid(int64_t n) {
 }
 
 hipError_t launch_amax_partials(const void* x, int hp, int64_t n, float* partials, int nparts,
-                                const fp8q_delayed_state* gate, hipStream_t s) {
+                                const fp8q_delayed_state* gate, hipStream_t s, uint32_t* keys,
+                                uint32_t* ctrs, float* amax_out) {
     const int vec = ((uintptr_t)x % 16) == 0;
     if (hp == FP8Q_BF16)
-        hipLaunchKernelGGL(amax_partials_kernel<FP8Q_BF16>, dim3(nparts), dim3(256), 0, s, x, n, partials, gate, vec);
+        hipLaunchKernelGGL(amax_partials_kernel<FP8Q_BF16>, dim3(nparts), dim3(256), 0, s, x, n, partials, gate, vec,
+                           keys, ctrs, amax_out);
     else
-        hipLaunchKernelGGL(amax_partials_kernel<FP8Q_F32>, dim3(nparts), dim3(256), 0, s, x, n, partials, gate, vec);
+        hipLaunchKernelGGL(amax_partials_kernel<FP8Q_F32>, dim3(nparts), dim3(256), 0, s, x, n, partials, gate, vec,
+                           keys, ctrs, amax_out);
     return hipGetLastError();
 }
 
-hipError_t launch_amax_finalize(const float* partials, int nparts, float* amax_out, hipStream_t s) {
-    hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(256), 0, s, partials, nparts, amax_out);
-    return hipGetLastError();
-}
 
 // ------------------------------------------------------------------ LDS tile transposes
 
@@ -301,14 +339,14 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(QuantArgs a, int64_
                 const int64_t row = r0 + rg + 16 * p;
                 float q[8];
                 if constexpr (SCHEME == kTileAxis0) {
-                    const uint32_t k = lanes_max_u32<1, 8>(kp[p]);
+                    const uint32_t k = row16_max_u32(kp[p]);
                     const float s = scale_from_amax<FMT>(__uint_as_float(k));
                     const float r = 1.0f / s;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(div_by_scale(v[p][e], s, r));
                     if (cc == 0 && row < rows) a.scales[row * nst + tc] = s;
                 } else {
-                    const uint32_t k = lanes_max_u32<1, 2>(kp[p]);
+                    const uint32_t k = quad_max_u32(kp[p]);
                     const int code = e8m0_from_scale(scale_from_amax<FMT>(__uint_as_float(k)));
                     const float inv = e8m0_recip(code);
 #pragma unroll
@@ -447,25 +485,22 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(QuantArgs a, int64_
         }
     } else if constexpr (SCHEME == kPerTensorDelayed) {
         // The grid's amax goes into the history after every block has cast with
-        // the old scale: integer atomic max, then the last block to arrive
-        // records it and resets the working fields.
+        // the old scale: the last block to finish folds the per-block maxima
+        // and records it.
+        __shared__ uint32_t last;
         const uint32_t k = block_max_u32_256(key_all, red);
-        if (t == 0) {
-            fp8q_delayed_state* st = a.state;
-            atomicMax(&st->amax_bits, k);
-            __threadfence();
-            const uint32_t prev = atomicAdd(&st->arrive, 1u);
-            if (prev == gridDim.x - 1) {
-                __threadfence();
-                const float amax = __uint_as_float(atomicOr(&st->amax_bits, 0u));
+        if (t == 0) last = grid_done(a.keys, a.ctrs, k);
+        __syncthreads();
+        if (last) {
+            const float amax = __uint_as_float(fold_keys_256(a.keys, gridDim.x, red));
+            if (t == 0) {
+                fp8q_delayed_state* st = a.state;
                 const int pos = st->pos;
                 st->amax_history[pos] = amax;
                 st->pos = (pos + 1) % FP8Q_HISTORY_LEN;
                 st->last_scale = s_pt;
                 *a.scale_out = s_pt;
                 if (a.amax_out) *a.amax_out = amax;
-                atomicExch(&st->amax_bits, 0u);
-                atomicExch(&st->arrive, 0u);
             }
         }
     }
@@ -504,6 +539,134 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
     }
 }
 
+// ------------------------------------------------------------------ flat quantize
+//
+// Row-major quantizers whose scale groups run along the rows (per tensor, 1x128
+// tiles, MX32 blocks along the columns) and with no transposed copy: the
+// tensor is streamed as a flat array of 8-element units (16 bytes of bf16, 32
+// of fp32).  Each block takes one contiguous run of units (a multiple of 256,
+// so a 1x128 tile - 16 units - or an MX block - 4 units - never straddles
+// blocks or lane groups), each thread keeps UNR units in flight, tile and MX
+// maxima are reduced across 16 or 4 neighbouring lanes, and every lane stores
+// its 8 codes as one 8-byte word.  The flat unit index also gives the scale
+// index directly: unit u belongs to 1x128 tile u / 16 and MX block u / 4.
+template <int HP>
+__device__ __forceinline__ void load_unit(const void* __restrict__ x, int64_t u, float v[8]) {
+    if constexpr (HP == FP8Q_BF16) {
+        const uint4 w = reinterpret_cast<const uint4*>(x)[u];
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(d[j] << 16);
+            v[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = reinterpret_cast<const float4*>(x)[2 * u];
+        const float4 b = reinterpret_cast<const float4*>(x)[2 * u + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+template <int HP, int FMT, int SCHEME, bool SAT>
+__global__ __launch_bounds__(256) void quantize_flat_kernel(QuantArgs a, int64_t nunits) {
+    constexpr int UNR = HP == FP8Q_BF16 ? 8 : 4;
+    constexpr bool kPerTensor = SCHEME == kPerTensorCurrent || SCHEME == kPerTensorDelayed;
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x;
+
+    float s_pt = 0.0f, r_pt = 0.0f, amax_pt = 0.0f;
+    if constexpr (SCHEME == kPerTensorCurrent) {
+        amax_pt = reduce_partials_256(a.partials, a.nparts, red);
+        s_pt = scale_from_amax<FMT>(amax_pt);
+    } else if constexpr (SCHEME == kPerTensorDelayed) {
+        uint32_t h = 0, any = 0;
+#pragma unroll
+        for (int i = 0; i < FP8Q_HISTORY_LEN; ++i) {
+            const uint32_t b = __float_as_uint(a.state->amax_history[i]);
+            any |= b;
+            const uint32_t k = b & 0x7fffffffu;
+            h = h > k ? h : k;
+        }
+        const bool cold = (any & 0x7fffffffu) == 0;
+        const float hmax = cold ? reduce_partials_256(a.partials, a.nparts, red) : __uint_as_float(h);
+        s_pt = scale_from_amax<FMT>(hmax);
+    }
+    if constexpr (kPerTensor) r_pt = 1.0f / s_pt;
+
+    const int64_t per = ((nunits + gridDim.x - 1) / gridDim.x + 255) / 256 * 256;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = b0 + per < nunits ? b0 + per : nunits;
+    uint32_t key_all = 0;
+    for (int64_t base = b0; base < b1; base += 256 * UNR) {
+        float v[UNR][8];
+        // units past the run's end re-read its last unit (loads stay
+        // unconditional); nothing of theirs is stored or counted
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const int64_t u = base + k * 256 + t;
+            load_unit<HP>(a.x, u < b1 ? u : b1 - 1, v[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const int64_t u = base + k * 256 + t;
+            const bool valid = u < b1;
+            uint32_t key = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { const uint32_t z = abs_key(v[k][e]); key = key > z ? key : z; }
+            float q[8];
+            if constexpr (kPerTensor) {
+                if constexpr (SCHEME == kPerTensorDelayed) key_all = valid && key > key_all ? key : key_all;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(div_by_scale(v[k][e], s_pt, r_pt));
+            } else if constexpr (SCHEME == kTileAxis0) {
+                key = row16_max_u32(key);
+                const float sc = scale_from_amax<FMT>(__uint_as_float(key));
+                const float r = 1.0f / sc;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(div_by_scale(v[k][e], sc, r));
+                if (valid && (t & 15) == 0) a.scales[u >> 4] = sc;
+            } else {   // kMxAxis0
+                key = quad_max_u32(key);
+                const int code = e8m0_from_scale(scale_from_amax<FMT>(__uint_as_float(key)));
+                const float inv = e8m0_recip(code);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(v[k][e] * inv);
+                if (valid && (t & 3) == 0) a.e8m0[u >> 2] = (uint8_t)code;
+            }
+            if (valid)
+                reinterpret_cast<uint2*>(a.q)[u] = make_uint2(pack4<FMT>(q[0], q[1], q[2], q[3]),
+                                                              pack4<FMT>(q[4], q[5], q[6], q[7]));
+        }
+    }
+
+    if constexpr (SCHEME == kPerTensorCurrent) {
+        if (blockIdx.x == 0 && t == 0) {
+            *a.scale_out = s_pt;
+            if (a.amax_out) *a.amax_out = amax_pt;
+        }
+    } else if constexpr (SCHEME == kPerTensorDelayed) {
+        // as in the tiled kernel: the last block to finish folds the per-block
+        // maxima and records the grid's amax in the history
+        __shared__ uint32_t last;
+        const uint32_t k = block_max_u32_256(key_all, red);
+        if (t == 0) last = grid_done(a.keys, a.ctrs, k);
+        __syncthreads();
+        if (last) {
+            const float amax = __uint_as_float(fold_keys_256(a.keys, gridDim.x, red));
+            if (t == 0) {
+                fp8q_delayed_state* st = a.state;
+                const int pos = st->pos;
+                st->amax_history[pos] = amax;
+                st->pos = (pos + 1) % FP8Q_HISTORY_LEN;
+                st->last_scale = s_pt;
+                *a.scale_out = s_pt;
+                if (a.amax_out) *a.amax_out = amax;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 
 static int tile_grid(int64_t ntiles) {
@@ -532,7 +695,49 @@ static void launch_q2(const QuantArgs& a, int grid, int64_t ntr, int64_t ntc, in
     }
 }
 
+template <int HP, int FMT, int SCHEME>
+static void launch_flat3(const QuantArgs& a, int64_t nunits, hipStream_t s) {
+    const int64_t g = (nunits + 2047) / 2048;   // >= 8 units per thread
+    const int grid = (int)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
+    if (a.saturate)
+        hipLaunchKernelGGL((quantize_flat_kernel<HP, FMT, SCHEME, true>), dim3(grid), dim3(256), 0, s, a, nunits);
+    else
+        hipLaunchKernelGGL((quantize_flat_kernel<HP, FMT, SCHEME, false>), dim3(grid), dim3(256), 0, s, a, nunits);
+}
+
+template <int HP, int FMT>
+static void launch_flat2(const QuantArgs& a, int64_t nunits, hipStream_t s) {
+    switch (a.scheme) {
+        case kPerTensorCurrent: launch_flat3<HP, FMT, kPerTensorCurrent>(a, nunits, s); break;
+        case kPerTensorDelayed: launch_flat3<HP, FMT, kPerTensorDelayed>(a, nunits, s); break;
+        case kTileAxis0: launch_flat3<HP, FMT, kTileAxis0>(a, nunits, s); break;
+        default: launch_flat3<HP, FMT, kMxAxis0>(a, nunits, s); break;
+    }
+}
+
+// The flat kernel serves row-direction schemes without a transposed copy when
+// 8-element units are 16-byte aligned and never straddle a row, and rows hold
+// whole 1x128 tiles (cols % 128 == 0) or MX blocks (cols % 32 == 0).
+static bool flat_ok(const QuantArgs& a) {
+    bool scheme = false;
+    if (a.scheme == kPerTensorCurrent || a.scheme == kPerTensorDelayed) scheme = a.cols % 8 == 0;
+    else if (a.scheme == kTileAxis0) scheme = a.cols % 128 == 0;
+    else if (a.scheme == kMxAxis0) scheme = a.cols % 32 == 0;
+    return scheme && a.qT == nullptr && a.q != nullptr && (uintptr_t)a.x % 16 == 0 && (uintptr_t)a.q % 8 == 0;
+}
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+    if (flat_ok(a)) {
+        const int64_t nunits = a.rows * a.cols / 8;
+        if (a.hp == FP8Q_BF16) {
+            if (a.fmt == FP8Q_E4M3) launch_flat2<FP8Q_BF16, FP8Q_E4M3>(a, nunits, s);
+            else launch_flat2<FP8Q_BF16, FP8Q_E5M2>(a, nunits, s);
+        } else {
+            if (a.fmt == FP8Q_E4M3) launch_flat2<FP8Q_F32, FP8Q_E4M3>(a, nunits, s);
+            else launch_flat2<FP8Q_F32, FP8Q_E5M2>(a, nunits, s);
+        }
+        return hipGetLastError();
+    }
     const int64_t ntr = (a.rows + kTile - 1) / kTile, ntc = (a.cols + kTile - 1) / kTile;
     const int grid = tile_grid(ntr * ntc);
     const int esz = a.hp == FP8Q_BF16 ? 2 : 4;

@@ -87,15 +87,16 @@ typedef enum fp8q_scaling { FP8Q_CURRENT = 0, FP8Q_DELAYED = 1 } fp8q_scaling;
 /*
  * Delayed-scaling state, in DEVICE memory, owned by the caller.  Create it
  * zero-filled (an all-zero history is a cold start, which uses the current
- * amax).  amax_bits and arrive are the library's working fields; every call
- * leaves them zero.  One state must not be used by two calls that may run
- * concurrently.  Saving amax_history and pos checkpoints the recipe.
+ * amax).  The grid-wide amax of a call is folded in the call's reduce
+ * workspace; amax_bits and arrive are reserved (keep them zero).  One state
+ * must not be used by two calls that may run concurrently.  Saving
+ * amax_history and pos checkpoints the recipe.
  */
 typedef struct fp8q_delayed_state {
     float amax_history[FP8Q_HISTORY_LEN]; /* amaxes of earlier steps (ring) */
     int32_t pos;                          /* next ring slot to write */
-    uint32_t amax_bits;                   /* working field, zero between calls */
-    uint32_t arrive;                      /* working field, zero between calls */
+    uint32_t amax_bits;                   /* reserved, zero */
+    uint32_t arrive;                      /* reserved, zero */
     float last_scale;                     /* scale used by the most recent call */
 } fp8q_delayed_state;
 
@@ -111,7 +112,11 @@ const char* fp8q_status_string(int status);
  * The string stays valid until the next call on this thread. */
 const char* fp8q_last_error(void);
 
-/* Bytes of device workspace the reductions need (amax partial maxima). */
+/* Bytes of device workspace the reductions need: amax partial maxima,
+ * per-block keys and completion counters.  The counters must be zero before
+ * the workspace's first use (zero-fill a new workspace once); every call
+ * leaves them at zero.  Calls that may overlap on the device must not share a
+ * workspace. */
 size_t fp8q_reduce_workspace_bytes(void);
 
 /* ---------------------------------------------------------------- amax */
@@ -119,8 +124,9 @@ size_t fp8q_reduce_workspace_bytes(void);
 /*
  * amax_out[0] = max_i |x_i| over n elements of type hp (NaN if any x_i is
  * NaN).  x: n elements, any alignment of the element type.  ws: at least
- * fp8q_reduce_workspace_bytes() bytes of scratch (contents ignored and
- * overwritten).  Lab page, scaled_roundtrip.
+ * fp8q_reduce_workspace_bytes() bytes (zero-filled before its first use;
+ * see fp8q_reduce_workspace_bytes).  One launch: the last block to finish
+ * folds the per-block maxima.  Lab page, scaled_roundtrip.
  */
 int fp8_amax(const void* x, int hp, int64_t n, float* amax_out,
              void* ws, size_t ws_bytes, void* stream);
@@ -137,7 +143,8 @@ int fp8_amax(const void* x, int hp, int64_t n, float* amax_out,
  * qT: optional (may be NULL) second copy of the codes transposed, [cols, rows]
  *   (the K-major operand of a dgrad or wgrad GEMM).
  * scale_out: required, receives s.  amax_out: optional, receives amax(x).
- * flags: 0 or FP8Q_SATURATE.  ws: fp8q_reduce_workspace_bytes() bytes.
+ * flags: 0 or FP8Q_SATURATE.  ws: fp8q_reduce_workspace_bytes() bytes,
+ * zero-filled before its first use (see fp8q_reduce_workspace_bytes).
  * state: required for DELAYED, ignored for CURRENT.
  * Lab page: scaled_roundtrip; smoke check [3] (delayed vs current).
  */
@@ -243,7 +250,10 @@ size_t fp8_gemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
  * module_filter_fn); K a multiple of 128 with TILE_1x128 / BLOCK_128x128
  * operands and of 32 with MX32.  Granularities: A and B each PER_TENSOR,
  * TILE_1x128 or BLOCK_128x128 in any combination, or both MX32.
- * ws: fp8_gemm_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * ws: fp8_gemm_workspace_bytes(...) bytes (may be NULL when that is 0),
+ * zero-filled before its first use: autocast operands reduce in it, and its
+ * completion counters must start at zero (every call leaves them at zero).
+ * Calls that may overlap on the device must not share a workspace.
  */
 int fp8_gemm_scaled_NT(int64_t M, int64_t N, int64_t K, const fp8q_operand* A,
                        const fp8q_operand* B, void* C, int c_dtype,

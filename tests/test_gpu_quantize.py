@@ -35,6 +35,18 @@ def test_amax(shape, dtype):
         assert fq.fp8_amax(xd).item() == oracle.amax(host_input(x.reshape(-1)[1:]))
 
 
+def test_amax_reused_workspace():
+    """One workspace across many calls (the completion counter resets itself),
+    sizes from one block to the full grid, both element types."""
+    announce("amax reused workspace")
+    ws = fq.reduce_workspace(dev())
+    for i, (n, dtype) in enumerate([(7, torch.float32), (1 << 20, torch.bfloat16), (15872 * 4096, torch.bfloat16),
+                                    (3 << 18, torch.float32), (5, torch.bfloat16)]):
+        x = workloads.quantize_tensor(rows=1, cols=n, seed=70 + i).to(dtype)
+        for _ in range(2):
+            assert fq.fp8_amax(x.to(dev()), ws=ws).item() == oracle.amax(host_input(x.reshape(-1)))
+
+
 def test_amax_nan_propagates():
     announce("amax nan")
     x = make((64, 512), torch.bfloat16, 11)
@@ -42,18 +54,22 @@ def test_amax_nan_propagates():
     assert np.isnan(fq.fp8_amax(x.to(dev())).item())
 
 
+# Without a transposed copy, row-major outputs with cols % 8 == 0 take the flat
+# streaming kernel; with one (or ragged cols) the 128 x 128 tiled kernel.
+@pytest.mark.parametrize("emit_t", [True, False])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("shape", SHAPES)
-def test_per_tensor_current(shape, dtype, fmt):
-    announce("per-tensor current", shape, dtype, fmt)
+@pytest.mark.parametrize("shape", SHAPES + [(7, 1000008)])
+def test_per_tensor_current(shape, dtype, fmt, emit_t):
+    announce("per-tensor current", shape, dtype, fmt, emit_t)
     x = make(shape, dtype, 20)
-    q, qT, s, a = fq.fp8_quantize_per_tensor(x.to(dev()), fmt, emit_t=True)
+    q, qT, s, a = fq.fp8_quantize_per_tensor(x.to(dev()), fmt, emit_t=emit_t)
     oq, os_, oa = oracle.quantize_per_tensor(host_input(x), fmt)
     oq = oq.reshape(shape)
     assert s.item() == os_ and a.item() == oa
     assert codes_equal(q.cpu().numpy(), oq, fmt)
-    assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
+    if emit_t:
+        assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -142,18 +158,20 @@ def test_delayed_full_size_spike():
         assert abs(v - 0.625) <= 0.625 * 2 ** -4
 
 
+@pytest.mark.parametrize("emit_t", [True, False])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("shape", [(3, 200), (300, 200), (257, 1030), (1000, 4096)])
-def test_tile1x128(shape, dtype, axis, fmt):
-    announce("tile1x128", shape, dtype, axis, fmt)
+@pytest.mark.parametrize("shape", [(3, 200), (300, 200), (257, 1030), (1000, 4096), (33, 3968)])
+def test_tile1x128(shape, dtype, axis, fmt, emit_t):
+    announce("tile1x128", shape, dtype, axis, fmt, emit_t)
     x = make(shape, dtype, 30)
-    q, qT, sc = fq.fp8_quantize_tile1x128(x.to(dev()), axis, fmt, emit_t=True)
+    q, qT, sc = fq.fp8_quantize_tile1x128(x.to(dev()), axis, fmt, emit_t=emit_t)
     oq, osc = oracle.quantize_tiles(host_input(x), axis, 128, fmt)
     assert scales_equal(sc.cpu().numpy(), osc)
     assert codes_equal(q.cpu().numpy(), oq, fmt)
-    assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
+    if emit_t:
+        assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -168,18 +186,20 @@ def test_block128x128(shape, fmt):
     assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
 
 
+@pytest.mark.parametrize("emit_t", [True, False])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("shape", [(3, 200), (300, 200), (257, 1030), (1000, 4096)])
-def test_mx32(shape, dtype, axis, fmt):
-    announce("mx32", shape, dtype, axis, fmt)
+@pytest.mark.parametrize("shape", [(3, 200), (300, 200), (257, 1030), (1000, 4096), (33, 3968)])
+def test_mx32(shape, dtype, axis, fmt, emit_t):
+    announce("mx32", shape, dtype, axis, fmt, emit_t)
     x = make(shape, dtype, 50)
-    q, qT, e8 = fq.fp8_quantize_mx32(x.to(dev()), axis, fmt, emit_t=True)
+    q, qT, e8 = fq.fp8_quantize_mx32(x.to(dev()), axis, fmt, emit_t=emit_t)
     oq, oe8 = oracle.quantize_tiles(host_input(x), axis, 32, fmt, mx=True)
     assert np.array_equal(e8.cpu().numpy(), oe8)
     assert codes_equal(q.cpu().numpy(), oq, fmt)
-    assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
+    if emit_t:
+        assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
 
 
 @pytest.mark.parametrize("kind", ["tile", "mx", "block"])

@@ -366,6 +366,23 @@ __device__ __forceinline__ void dload_tile(const uint8_t* __restrict__ base, con
                                          16, 0, 0);
 }
 
+// The same loads in compact form for the buffer (bounds-checked) load: the
+// chunk swizzle of instruction u depends on u only through its parity, so a
+// lane keeps two offsets - row base (row0 + 64 wave + l/8) * K plus the
+// swizzled chunk for even and for odd u - and instruction u adds u * 8 * K.
+// Nothing is clamped: rows past the matrix edge give offsets past the
+// buffer's end, which the buffer load returns as zeros.
+struct DmaB {
+    uint32_t e, o;
+};
+
+__device__ __forceinline__ DmaB dmab_plan(int64_t K, int64_t row0, int wave) {
+    const int l = threadIdx.x & 63;
+    const int64_t rb = (row0 + wave * 64 + (l >> 3)) * K;
+    const int ce = (l & 7) ^ (l >> 4), co = (l & 7) ^ (4 + (l >> 4));
+    return DmaB{(uint32_t)(rb + ce * 16), (uint32_t)(rb + co * 16)};
+}
+
 // s_waitcnt lgkmcnt(n) (vmcnt, expcnt at their maxima) for an n that is a
 // compile-time constant after unrolling; n above 15 waits for 15, which is
 // at least as strong since LDS reads complete in order.
@@ -417,9 +434,24 @@ __device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rsrc, uint32_t vo
 constexpr int kEpPitch = 272;     // bytes per staged bf16 row of 128 values (+16: conflict-free)
 constexpr int kEpPitch32 = 528;   // bytes per staged fp32 row of 128 values (+16)
 
-template <int FA, int FB, int OUT>
+// MX (SM == kSmMx, K % 512 == 0): the E8M0 scales travel to LDS in groups of
+// four K steps: for each tile row, 16 bytes = its four 32-K blocks of four
+// consecutive K steps, one 16-byte direct-to-LDS load per lane (64 rows per
+// instruction), double-buffered by group and loaded one group ahead.  Right
+// after each barrier every lane reads the byte of its fragment rows and 32-K
+// block for all 16 fragments of the new step, and the MFMAs take them as
+// their scale operands.  The scales of the row pair that runs after the
+// barrier are kept from the previous step.
+template <int FA, int FB, int OUT, int SM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int ntm, int ntn) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_ab[2][2 * kTileBytes];
+    constexpr bool MX = SM == kSmMx;
+    // One LDS allocation with the operand stages at offset 0 and the MX scale
+    // groups after them (with the compiler free to place a separate scale
+    // array first, the same kernel ran about 3x slower).
+    constexpr int kScaleGroupBytes = 2 * 256 * 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[2 * 2 * kTileBytes + (MX ? 2 * kScaleGroupBytes : 0)];
+    uint8_t(*lds_ab)[2 * kTileBytes] = reinterpret_cast<uint8_t(*)[2 * kTileBytes]>(lds_all);
+    uint8_t(*lds_sc)[kScaleGroupBytes] = reinterpret_cast<uint8_t(*)[kScaleGroupBytes]>(lds_all + 2 * 2 * kTileBytes);
     const int64_t M = g.M, N = g.N, K = g.K;
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
     const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
@@ -434,34 +466,94 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
     const int wave = __builtin_amdgcn_readfirstlane(w);
     int tm, tn;
     tile_coords(logical, ntm, ntn, tm, tn);
-    Dma2 da = dma2_plan(M, K, (int64_t)tm * BM, wave), db = dma2_plan(N, K, (int64_t)tn * 256, wave);
-    dload_tile(g.A, da, lds_ab[0], wave);
-    dload_tile(g.B, db, lds_ab[0] + kTileBytes, wave);
-    const float S = reinterpret_cast<const float*>(g.sa.s)[0] * reinterpret_cast<const float*>(g.sb.s)[0];
+    const uint32_t K32 = (uint32_t)K;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.A, M * K), rb = buffer_rsrc(g.B, N * K);
+    DmaB da = dmab_plan(K, (int64_t)tm * BM, wave), db = dmab_plan(K, (int64_t)tn * 256, wave);
+    // instruction u of a tile's loads at K offset ko (both in the lane offset,
+    // so the bounds check covers them)
+    auto tile_load = [&](const __amdgpu_buffer_rsrc_t& rs, const DmaB& p, uint32_t ko, uint8_t* dst, int u) {
+        dma_one(rs, ((u & 1) ? p.o : p.e) + (uint32_t)(u * 8) * K32 + ko, 0u, dst + (wave * 64 + u * 8) * BK);
+    };
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        tile_load(ra, da, 0u, lds_ab[0], u);
+        tile_load(rb, db, 0u, lds_ab[0] + kTileBytes, u);
+    }
+    // MX scale rows of this wave's loads: rows 64 * wave + lane of the A and B
+    // tiles (rows past the edge read as zeros, like the operands)
+    const uint32_t sld = (uint32_t)(K / 32);   // bytes per scale row
+    auto srow = [&](int64_t row0) { return (uint32_t)((row0 + wave * 64 + l) * sld); };
+    uint32_t sa_off = 0, sb_off = 0, nsa_off = 0, nsb_off = 0;
+    // (per-tensor mode: descriptors over the scalar scales, never used)
+    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(g.sa.s, MX ? M * (K / 32) : 4);
+    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(g.sb.s, MX ? N * (K / 32) : 4);
+    const int ngroups = (nk + 3) / 4;   // MX scale groups of four K steps
+    int gpar = 0;                       // group gi of the current tile lives in scale buffer (gi + gpar) % 2
+    // 16-byte loads of scale group gi of this wave's A and B rows into buffer `buf`
+    auto load_group = [&](int buf, uint32_t aoff, uint32_t boff, int gi) {
+        uint8_t* st = lds_sc[buf];
+        dma_one(rsa, aoff + (uint32_t)gi * 16, 0u, st + wave * 64 * 16);
+        dma_one(rsb, boff + (uint32_t)gi * 16, 0u, st + 4096 + wave * 64 * 16);
+    };
+    if constexpr (MX) {
+        sa_off = srow((int64_t)tm * BM);
+        sb_off = srow((int64_t)tn * 256);
+        load_group(0, sa_off, sb_off, 0);
+    }
+    const float S = MX ? 1.0f : reinterpret_cast<const float*>(g.sa.s)[0] * reinterpret_cast<const float*>(g.sb.s)[0];
 
     v4f acc[8][8];
     v8i b[8];
     v8i ax[2], ay[2];
-    Dma2 na, nb;
+    DmaB na{0u, 0u}, nb{0u, 0u};
+    int sa[8], sb[8];         // MX: this step's E8M0 bytes for A rows 16i.. and B rows 16j..
+    int sa_o[2], sb_o[8];     // MX: the previous step's, for its rows 6, 7
+    int sa_n[8], sb_n[8];     // MX: the next step's, read during this one
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sa[i] = sb[i] = sb_o[i] = sa_n[i] = sb_n[i] = 127;
+    sa_o[0] = sa_o[1] = 127;
 
+    // MFMA of A fragment row i, B fragment column j; sbv / sav are the E8M0
+    // scale bytes (MX) of the B and A rows of this lane
+    auto mfma_s = [&](int i, const v8i& bb, const v8i& a, int j, int sbv, int sav) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bb, a, acc[i][j], kFmtB, kFmtA, 0, sbv, 0, sav);
+    };
     auto mfma = [&](int i, const v8i& bb, const v8i& a, int j) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bb, a, acc[i][j], kFmtB, kFmtA, 0, 0, 0, 0);
+        if constexpr (MX) mfma_s(i, bb, a, j, sb[j], sa[i]);
+        else mfma_s(i, bb, a, j, 0, 0);
     };
     // Stage kt of the current tile lives in buffer (kt + par) % 2.  Load slot
     // u (0..15) of a wave: MODE 1 = stage kt+1 of this tile, MODE 2 = stage 0
     // of the next tile; both go to the buffer the current step does not read.
     int par = 0;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.A, M * K), rb = buffer_rsrc(g.B, N * K);
     auto dma = [&](auto mode_c, int kt, int u) {
         constexpr int MODE = decltype(mode_c)::value;
         const uint32_t ko = MODE == 1 ? (uint32_t)(kt + 1) * BK : 0u;
         uint8_t* dst = lds_ab[(kt + 1 + par) & 1];
-        const Dma2& pa = MODE == 1 ? da : na;
-        const Dma2& pb = MODE == 1 ? db : nb;
-        if (u < 8) dma_one(ra, pa.off[u], ko, dst + (wave * 64 + u * 8) * BK);
-        else dma_one(rb, pb.off[u - 8], ko, dst + kTileBytes + (wave * 64 + (u - 8) * 8) * BK);
+        if (u < 8) {
+            tile_load(ra, MODE == 1 ? da : na, ko, dst, u);
+        } else if (u < 16) {
+            tile_load(rb, MODE == 1 ? db : nb, ko, dst + kTileBytes, u - 8);
+        } else if constexpr (MX) {   // u = 16: the next scale group of this tile, or the next tile's first
+            if (MODE == 1) {
+                if (kt % 4 == 0 && kt / 4 + 1 < ngroups) load_group((kt / 4 + 1 + gpar) & 1, sa_off, sb_off, kt / 4 + 1);
+            } else {
+                load_group(((nk - 1) / 4 + 1 + gpar) & 1, nsa_off, nsb_off, 0);
+            }
+        }
     };
 
+    // MX: this lane's E8M0 bytes of K step kt (its 32-K block l/16) for the
+    // 8 A and 8 B fragment rows; one base per operand, row i 256 bytes on
+    auto read_scales = [&](int kt, int (&ra_)[8], int (&rb_)[8]) {
+        const uint8_t* grp = lds_sc[(kt / 4 + gpar) & 1] + 4 * (kt % 4) + (l >> 4);
+        const uint8_t* spa = grp + (wm + (l & 15)) * 16;
+        const uint8_t* spb = grp + 4096 + (wn + (l & 15)) * 16;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ra_[i] = spa[256 * i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rb_[j] = spb[256 * j];
+    };
     // Half-fragment read: h = 0 brings K bytes [16g, 16g+16) of the lane's
     // row, h = 1 bytes [64+16g, 64+16g+16) (g = lane / 16).
     auto rdh = [&](v8i& f, const uint8_t* p, int r0, int h) {
@@ -483,14 +575,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
         constexpr bool DEFERRED = decltype(deferred_c)::value;
         const uint8_t* la = lds_ab[(kt + par) & 1];
         const uint8_t* lb = la + kTileBytes;
+        if constexpr (MX) {
+            if constexpr (DEFERRED) {
+                // the previous step read this step's scale bytes
+#pragma unroll
+                for (int i = 0; i < 2; ++i) sa_o[i] = sa[6 + i];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sb_o[j] = sb[j];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sa[i] = sa_n[i];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sb[j] = sb_n[j];
+            } else {
+                // a tile's first step reads its own, before every fragment
+                // read so that the waits below cover them too
+                read_scales(kt, sa, sb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // previous step's rows 6, 7 (column-major, registers only) while
         // reads 0-15 go out; b[j] is re-read only after its last old use
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            if constexpr (DEFERRED) mfma(6 + (q & 1), b[q >> 1], ay[q & 1], q >> 1);
+            if constexpr (DEFERRED) {
+                if constexpr (MX) mfma_s(6 + (q & 1), b[q >> 1], ay[q & 1], q >> 1, sb_o[q >> 1], sa_o[q & 1]);
+                else mfma(6 + (q & 1), b[q >> 1], ay[q & 1], q >> 1);
+            }
             if (q < 4) rdh(ax[q >> 1], la, wm + 16 * (q >> 1), q & 1);
             else rdh(b[(q - 4) >> 1], lb, wn + 16 * ((q - 4) >> 1), q & 1);
             if (MODE && (q & 1)) dma(mode_c, kt, q >> 1);
+            if (MX && MODE && q == 0) dma(mode_c, kt, 16);
             __builtin_amdgcn_sched_barrier(0);
         }
         // rows 0, 1 (column-major); reads 16-23
@@ -518,15 +632,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
             if (m < 4) rdh(ax[m >> 1], la, wm + 64 + 16 * (m >> 1), m & 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // rows 4, 5; reads 28-31
+        // rows 4, 5; reads 28-31 (MX: then the next step's 16 scale bytes,
+        // which only the end-of-step wait covers)
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int j = m & 7, i = m >> 3;
-            const int issued = 28 + (m < 4 ? m : 4);
+            const int issued = 28 + (m < 4 ? m : 4) + (MX && MODE == 1 && m > 8 ? 16 : 0);
             lgkm_wait(issued - (i == 0 ? 25 : 27) - 1);
             __builtin_amdgcn_sched_barrier(0);
             mfma(4 + i, b[j], ax[i], j);
             if (m < 4) rdh(ay[m >> 1], la, wm + 96 + 16 * (m >> 1), m & 1);
+            if (MX && MODE == 1 && m == 8) read_scales(kt + 1, sa_n, sb_n);
             __builtin_amdgcn_sched_barrier(0);
         }
         // this stage fully read; the next stage of this tile landed (the next
@@ -556,13 +672,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
         stage_barrier();
         step(C1{}, F{}, 0);
         for (int kt = 1; kt + 1 < nk; ++kt) step(C1{}, T{}, kt);
-        na = dma2_plan(M, K, (int64_t)ntm_ * BM, wave);
-        nb = dma2_plan(N, K, (int64_t)ntn_ * 256, wave);
+        na = dmab_plan(K, (int64_t)ntm_ * BM, wave);
+        nb = dmab_plan(K, (int64_t)ntn_ * 256, wave);
+        if constexpr (MX) {
+            nsa_off = srow((int64_t)ntm_ * BM);
+            nsb_off = srow((int64_t)ntn_ * 256);
+        }
         step(C2{}, T{}, nk - 1);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             mfma(6, b[j], ay[0], j);
             mfma(7, b[j], ay[1], j);
+        }
+        if constexpr (MX) {
+            // keep the last MFMAs here: left free, the compiler sinks them
+            // into the epilogue's store branches and spills the fragments
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
         }
 
         const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 256;
@@ -616,10 +744,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
         if (!has_next) break;
         logical = next;
         par = (nk + par) & 1;
+        gpar = (ngroups + gpar) & 1;
         tm = ntm_;
         tn = ntn_;
         da = na;
         db = nb;
+        sa_off = nsa_off;
+        sb_off = nsb_off;
     }
     // the last step's extra loads land before the workgroup's LDS is released
     vm_wait<0>();
@@ -648,9 +779,16 @@ static void launch_sm(const GemmArgs& g, int sm, hipStream_t s) {
         return;
     }
     const int ntn = (int)((g.N + 255) / 256);
-    const bool offsets32 = g.M * g.K <= (int64_t(1) << 32) && g.N * g.K <= (int64_t(1) << 32);
-    if (sm == kSmPerTensor && g.K % BK == 0 && g.K >= 2 * BK && offsets32)
-        hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT>), dim3(persistent_grid()), dim3(kThreads), 0, s, g, ntm, ntn);
+    // lane offsets, K offset included, stay below 2^32 (rows past the edge may
+    // wrap; the buffer load's bounds check then returns zeros or in-range bytes)
+    const bool offsets32 = g.M * g.K < (int64_t(1) << 32) && g.N * g.K < (int64_t(1) << 32);
+    const bool fast = g.K % BK == 0 && g.K >= 2 * BK && offsets32;
+    if (sm == kSmPerTensor && fast)
+        hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmPerTensor>), dim3(persistent_grid()), dim3(kThreads), 0, s,
+                           g, ntm, ntn);
+    else if (sm == kSmMx && fast && g.K % 512 == 0)
+        hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmMx>), dim3(persistent_grid()), dim3(kThreads), 0, s, g,
+                           ntm, ntn);
     else if (sm == kSmPerTensor)
         hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmPerTensor, 256>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
     else

@@ -189,8 +189,11 @@ def test_block_scaled(op, shape):
     assert gemm_close(Ca, ref, torch.float32)
 
 
+# K = 128 or K % 128 != 0: the register-staged kernel; K >= 256 with K % 128 == 0
+# (here 3, 8 and 9 K steps, ragged M and N): the persistent kernel's MX mode.
 @pytest.mark.parametrize("op", ["NT", "NN", "TN"])
-@pytest.mark.parametrize("shape", [(256, 256, 128), (528, 400, 96), (1024, 1536, 1024)])
+@pytest.mark.parametrize("shape", [(256, 256, 128), (528, 400, 96), (1024, 1536, 1024), (1040, 784, 384),
+                                   (784, 1040, 1152)])
 def test_mx32(op, shape):
     M, N, K = shape
     announce("gemm mx32", op, shape)
@@ -208,6 +211,27 @@ def test_mx32(op, shape):
     assert gemm_close(C, ref, torch.float32)
     Ca = GEMM[op](M, N, K, AC(A.to(dev()), fa, fq.MX32), AC(B.to(dev()), fb, fq.MX32), torch.float32)
     assert gemm_close(Ca, ref, torch.float32)
+
+
+@pytest.mark.parametrize("op", ["NT", "TN"])
+def test_mx32_persistent_multi_tile(op):
+    """MX32 with more output tiles than workgroups and an odd K-step count:
+    sampled rows (tile edges included) against the oracle."""
+    M, N, K = 4112, 4112, 384
+    announce("gemm mx32 multi-tile", op)
+    A, B = block_operands(op, M, N, K, seed=350)
+    fa, fb = (fq.E5M2, fq.E4M3) if op != "NT" else (fq.E4M3, fq.E4M3)
+    axa = 0 if kcontig(op, "A") else 1
+    axb = 0 if kcontig(op, "B") else 1
+    qa, qaT, ea = fq.fp8_quantize_mx32(A.to(dev()), axa, fa, emit_t=axa == 1)
+    qb, qbT, eb = fq.fp8_quantize_mx32(B.to(dev()), axb, fb, emit_t=axb == 1)
+    oqa, oea = oracle.quantize_tiles(host_input(A), axa, 32, fa, mx=True)
+    oqb, oeb = oracle.quantize_tiles(host_input(B), axb, 32, fb, mx=True)
+    rows = sample_rows(M, seed=M + K + 1)
+    ref = OGEMM[op](oqa, oqb, fa, fb, oracle.Scale("rowk", oea, kblk=32, e8m0=True),
+                    oracle.Scale("rowk", oeb, kblk=32, e8m0=True), rows=rows)
+    C = GEMM[op](M, N, K, Q(qa, fa, ea, fq.MX32, kmajor=qaT), Q(qb, fb, eb, fq.MX32, kmajor=qbT), torch.bfloat16)
+    assert gemm_close(C[torch.as_tensor(rows, device=C.device)], ref, torch.bfloat16)
 
 
 def test_gemm_reruns_bitwise_identical():

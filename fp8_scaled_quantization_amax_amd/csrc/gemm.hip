@@ -35,17 +35,11 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace fp8q {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int BM = 256, BK = 128;
-constexpr int kThreads = 256;
-constexpr int kTileBytes = BM * BK;     // the A tile of one stage (B takes BN * BK)
 
 enum ScaleMode : int { kSmPerTensor = 0, kSmBlock = 1, kSmMx = 2 };
 
@@ -298,91 +292,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, int ntm, 
 //    buffer the last step read, and stored as 16-byte row-contiguous pieces,
 //    so each store instruction writes whole cache lines.
 
-// Swizzle of the 16-byte chunks of a 128-byte LDS row: chunk c of row r sits
-// at c ^ ((r / 2) % 8).  A fragment read serves 16 consecutive rows at one
-// logical chunk per phase; the XOR spreads them over 8 chunk positions x 2
-// row parities, i.e. over all 64 banks.
-__device__ __forceinline__ int swz2(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 4); }
-
-// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima): every LDS
-// read issued so far has landed.
-__device__ __forceinline__ void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Workgroup barrier for the staged pipeline.  Each wave has already waited
-// for its own loads of the stage about to be read (vm_wait) and for its own
-// LDS reads of the stage about to be overwritten (lds_wait_all), so only the
-// execution barrier is needed; __syncthreads() would add a full vmcnt(0)
-// wait.  The empty asm keeps the compiler from moving memory accesses across.
-__device__ __forceinline__ void stage_barrier() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N) with lgkmcnt and expcnt at their maxima (vmcnt is six
-// bits: [3:0] and [15:14] of the immediate); N < 64.
-template <int N>
-__device__ __forceinline__ void vm_wait() { __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14)); }
-
-__device__ __forceinline__ v8i frag2(const uint8_t* lds, int r0) {
-    const int l = threadIdx.x & 63;
-    const int r = r0 + (l & 15), g = l >> 4;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz2(r, g));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz2(r, g + 4));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// Direct global -> LDS loads of one 256 x 128 operand tile: wave w brings rows
-// [64w, 64w+64) in 8 instructions of 8 rows.  The hardware writes lane l's 16
-// bytes at the instruction's LDS base + 16 l, i.e. row l/8, physical chunk
-// l%8 of the 8-row group; the lane therefore fetches the logical chunk that
-// the swizzle places there.  Rows past the matrix edge re-read the last row
-// (their products only reach outputs that are never stored).  The per-lane
-// offsets are computed once per tile; a step moves the base pointer by its K
-// offset, and the LDS destination (M0) is scalar arithmetic on the wave index.
-struct Dma2 {
-    uint32_t off[8];
-};
-
-__device__ __forceinline__ Dma2 dma2_plan(int64_t nrows, int64_t K, int64_t row0, int wave) {
-    const int l = threadIdx.x & 63;
-    Dma2 d;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int r = wave * 64 + u * 8 + (l >> 3);
-        const int c = (l & 7) ^ ((r >> 1) & 7);
-        int64_t row = row0 + r;
-        row = row < nrows ? row : nrows - 1;
-        d.off[u] = (uint32_t)(row * K + c * 16);
-    }
-    return d;
-}
-
-__device__ __forceinline__ void dload_tile(const uint8_t* __restrict__ base, const Dma2& d, uint8_t* lds, int wave) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        __builtin_amdgcn_global_load_lds(base + d.off[u],
-                                         (__attribute__((address_space(3))) void*)(lds + (wave * 64 + u * 8) * BK),
-                                         16, 0, 0);
-}
-
-// The same loads in compact form for the buffer (bounds-checked) load: the
-// chunk swizzle of instruction u depends on u only through its parity, so a
-// lane keeps two offsets - row base (row0 + 64 wave + l/8) * K plus the
-// swizzled chunk for even and for odd u - and instruction u adds u * 8 * K.
-// Nothing is clamped: rows past the matrix edge give offsets past the
-// buffer's end, which the buffer load returns as zeros.
-struct DmaB {
-    uint32_t e, o;
-};
-
-__device__ __forceinline__ DmaB dmab_plan(int64_t K, int64_t row0, int wave) {
-    const int l = threadIdx.x & 63;
-    const int64_t rb = (row0 + wave * 64 + (l >> 3)) * K;
-    const int ce = (l & 7) ^ (l >> 4), co = (l & 7) ^ (4 + (l >> 4));
-    return DmaB{(uint32_t)(rb + ce * 16), (uint32_t)(rb + co * 16)};
-}
-
 // s_waitcnt lgkmcnt(n) (vmcnt, expcnt at their maxima) for an n that is a
 // compile-time constant after unrolling; n above 15 waits for 15, which is
 // at least as strong since LDS reads complete in order.
@@ -405,30 +314,6 @@ __device__ __forceinline__ void lgkm_wait(int n) {
         case 14: __builtin_amdgcn_s_waitcnt(0xCE7F); break;
         default: __builtin_amdgcn_s_waitcnt(0xCF7F); break;
     }
-}
-
-// Logical tile lg -> (tm, tn): groups of 8 M-tiles, N-tiles walked inside a group.
-__device__ __forceinline__ void tile_coords(int lg, int ntm, int ntn, int& tm, int& tn) {
-    constexpr int GM = 8;
-    const int per_group = GM * ntn;
-    const int group = lg / per_group;
-    const int first_m = group * GM;
-    const int gsize = ntm - first_m < GM ? ntm - first_m : GM;
-    const int in_group = lg % per_group;
-    tm = first_m + in_group % gsize;
-    tn = in_group / gsize;
-}
-
-// Raw buffer descriptor over [p, p + bytes) (bytes clamped to 2^32 - 1) for
-// the buffer form of the direct-to-LDS load: per-lane 32-bit offset in a
-// VGPR, per-step K offset in an SGPR, so no 64-bit address arithmetic.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int64_t bytes) {
-    const int64_t n = bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)(uint32_t)n, 0x00020000);
-}
-
-__device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint8_t* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
 constexpr int kEpPitch = 272;     // bytes per staged bf16 row of 128 values (+16: conflict-free)
@@ -756,33 +641,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
     vm_wait<0>();
 }
 
-// Workgroups of the persistent kernel: one per CU, rounded down to a multiple
-// of the 8 XCDs (the kernel splits the tiles into 8 per-XCD ranges).
-static int persistent_grid() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
-        cached[dev] = cus / 8 * 8;
-    }
-    return cached[dev];
-}
-
 template <int FA, int FB, int OUT>
 static void launch_sm(const GemmArgs& g, int sm, hipStream_t s) {
     const int ntm = (int)((g.M + BM - 1) / BM);
-    if (sm == kSmBlock) {
-        const int ntn = (int)((g.N + 127) / 128);
-        hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmBlock, 128>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
-        return;
-    }
-    const int ntn = (int)((g.N + 255) / 256);
     // lane offsets, K offset included, stay below 2^32 (rows past the edge may
     // wrap; the buffer load's bounds check then returns zeros or in-range bytes)
     const bool offsets32 = g.M * g.K < (int64_t(1) << 32) && g.N * g.K < (int64_t(1) << 32);
     const bool fast = g.K % BK == 0 && g.K >= 2 * BK && offsets32;
+    if (sm == kSmBlock) {
+        if (launch_gemm_block_persistent(g, s)) return;
+        const int ntn = (int)((g.N + 127) / 128);
+        hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmBlock, 128>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm,
+                           ntn);
+        return;
+    }
+    const int ntn = (int)((g.N + 255) / 256);
     if (sm == kSmPerTensor && fast)
         hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmPerTensor>), dim3(persistent_grid()), dim3(kThreads), 0, s,
                            g, ntm, ntn);

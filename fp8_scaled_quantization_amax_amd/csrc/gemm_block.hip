@@ -1,0 +1,323 @@
+// Block-scaled FP8 GEMM (1x128 activation / gradient tiles with 128x128
+// weight blocks, or 1x128 tiles on both wgrad operands): persistent kernel.
+// Every 128-K block gets its own partial product, which is scaled by
+// sA(m, kb) * sB(n, kb) and added to fp32 accumulators.
+//
+// This file is compiled with MFMA results placed in VGPRs, where the FMAs
+// that add each K block's partial can read them directly (the other GEMM
+// kernels keep their accumulators in AGPRs).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gemm_common.h"
+#include "launch.h"
+
+namespace fp8q {
+
+// 1x128 row scales on A, and on B either 128x128 block scales (fprop / dgrad
+// weights) or 1x128 row scales (wgrad operands); K a multiple of 512.  Each
+// 16x16x128 MFMA covers exactly one 128-K block, so it runs with a zero
+// accumulator and its result is added into the fp32 accumulators with one
+// FMA per value: acc += (sA(m, kb) * sB(n, kb)) * partial.  Those FMAs need
+// the accumulators in VGPRs, so a wave owns 128 x 64 outputs (128 VGPRs) and
+// the workgroup tile is 256 x 128.  The rest follows the per-tensor kernel:
+// per-XCD tile ranges, direct-to-LDS operand loads one stage ahead (the last
+// K step of a tile loads the next tile's first stage), LDS-staged
+// row-contiguous stores.
+//  * Row scales travel like the MX exponents: 16 bytes per row (four K
+//    blocks) per direct-to-LDS load, one group of four K steps ahead, double
+//    buffered; one 64-row load per wave per group instead of a scattered
+//    4-byte load per fragment row and step (those cost about as much as the
+//    FMAs themselves).
+//  * With block-scaled B the 64 columns of a wave share one scale per K
+//    block (one uniform load per step, a step ahead), so the FMA factor is
+//    one product per fragment row and step.
+//  * The FMAs of fragment row i run under the MFMAs of row i + 1; those of
+//    the last row wait until after the next barrier.
+// bytes spanned by a fp32 scale array (rows >> rshift, ld, kstride) over nkb K blocks
+__device__ __forceinline__ int64_t scale_bytes(const GemmScale& s, int64_t rows, int64_t nkb) {
+    return ((((rows - 1) >> s.rshift) * s.ld + (nkb - 1) * s.kstride) + 1) * 4;
+}
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, 0, 0));
+}
+
+template <int FA, int FB, int OUT, bool BROW>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int ntm, int ntn) {
+    constexpr int BNb = 128;
+    constexpr int kStage = kTileBytes + BNb * BK;   // A 256 x 128 + B 128 x 128 bytes
+    constexpr int kScA = BM * 16, kScGroup = kScA + (BROW ? BNb * 16 : 0);
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[2 * kStage + 2 * kScGroup];
+    uint8_t* const lds_sc = lds_all + 2 * kStage;
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int t = threadIdx.x, l = t & 63, w = t >> 6;
+    const int wm = (w >> 1) * 128, wn = (w & 1) * 64;
+    constexpr int kFmtA = FA == FP8Q_E4M3 ? 0 : 1;
+    constexpr int kFmtB = FB == FP8Q_E4M3 ? 0 : 1;
+    const int nt = ntm * ntn;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per = gridDim.x / 8;
+    const int lo = (int)((int64_t)nt * xcd / 8), hi = (int)((int64_t)nt * (xcd + 1) / 8);
+    int logical = lo + slot;
+    if (logical >= hi) return;
+    const int nk = (int)(K / BK);
+    const int ngroups = nk / 4;
+    const int wave = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t K32 = (uint32_t)K;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.A, M * K), rb = buffer_rsrc(g.B, N * K);
+    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(g.sa.s, scale_bytes(g.sa, M, nk));
+    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(g.sb.s, scale_bytes(g.sb, N, nk));
+    const uint32_t lda4 = (uint32_t)(g.sa.ld * 4), ldb4 = (uint32_t)(g.sb.ld * 4);
+    const uint32_t ksb4 = (uint32_t)(g.sb.kstride * 4);
+
+    // per-tile state: DMA plans; byte offsets of the scale rows this wave
+    // stages (A rows 64 wave + lane; B rows likewise, waves 0 and 1), or of
+    // the wave's B block scale for K block 0
+    struct TileState {
+        DmaB a, b;
+        uint32_t sa_row, sb_row;
+    };
+    auto tile_state = [&](int lg) {
+        int tm, tn;
+        tile_coords(lg, ntm, ntn, tm, tn);
+        const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNb;
+        TileState s;
+        s.a = dmab_rows(K, m0 + 64 * wave);
+        s.b = dmab_rows(K, n0 + 32 * wave);
+        s.sa_row = (uint32_t)(m0 + 64 * wave + l) * lda4;
+        if constexpr (BROW) {
+            s.sb_row = (uint32_t)(n0 + 64 * wave + l) * ldb4;
+        } else {
+            const int64_t nb = (n0 + wn) >> 7, nb_last = (N - 1) >> 7;
+            s.sb_row = (uint32_t)(nb < nb_last ? nb : nb_last) * ldb4;
+        }
+        return s;
+    };
+    // load instruction u (0..11) of a stage: 8 of A rows, then 4 of B rows
+    auto stage_load = [&](const TileState& s, uint32_t ko, uint8_t* dst, int u) {
+        if (u < 8)
+            dma_one(ra, ((u & 1) ? s.a.o : s.a.e) + (uint32_t)(u * 8) * K32 + ko, 0u, dst + (wave * 64 + u * 8) * BK);
+        else
+            dma_one(rb, (((u - 8) & 1) ? s.b.o : s.b.e) + (uint32_t)((u - 8) * 8) * K32 + ko, 0u,
+                    dst + kTileBytes + (wave * 32 + (u - 8) * 8) * BK);
+    };
+    // scale group gi (K blocks 4 gi .. 4 gi + 3: 16 bytes per row) into buffer buf
+    auto group_load = [&](const TileState& s, int buf, int gi) {
+        uint8_t* dst = lds_sc + buf * kScGroup;
+        dma_one(rsa, s.sa_row + (uint32_t)gi * 16, 0u, dst + wave * 64 * 16);
+        if constexpr (BROW) {
+            if (wave < 2) dma_one(rsb, s.sb_row + (uint32_t)gi * 16, 0u, dst + kScA + wave * 64 * 16);
+        }
+    };
+    float sbn = 0.f;   // block-scaled B: the wave's scale of the next K step
+
+    TileState cur = tile_state(logical);
+#pragma unroll
+    for (int u = 0; u < 12; ++u) stage_load(cur, 0u, lds_all, u);
+    group_load(cur, 0, 0);
+    if constexpr (!BROW) sbn = load_f32(rsb, cur.sb_row);
+
+    constexpr int NSB = BROW ? 16 : 1;
+    v4f acc[8][4];
+    int par = 0, gpar = 0;
+    while (true) {
+        const int next = logical + per;
+        const bool has_next = next < hi;
+        // without a next tile the last step re-loads this tile's first stage
+        // into the free buffer: harmless, and it keeps the step branch-free
+        const TileState nxt = tile_state(has_next ? next : logical);
+        // p: the MFMA partials of fragment rows of parity 0 / 1.  Row 7's
+        // are added after the next barrier, under the next step's first
+        // fragment reads; before the first step they are zero.
+        v4f p[2][4];
+        float sf7 = 0.f, sb7[NSB];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[1][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < NSB; ++q) sb7[q] = 0.f;
+        auto row_fma = [&](int i, float s, const float* sb) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] = __builtin_fmaf(p[i & 1][j][r], BROW ? s * sb[4 * j + r] : s, acc[i][j][r]);
+        };
+        for (int kt = 0; kt < nk; ++kt) {
+            // this stage and its scales landed; every wave is done with the other buffers
+            vm_wait<0>();
+            stage_barrier();
+            const bool last = kt + 1 == nk;
+            const int gi = kt >> 2;
+            // scale groups: the next one of this tile at a group's first step,
+            // the next tile's first one at the last step
+            if (last) group_load(nxt, (ngroups + gpar) & 1, 0);
+            else if ((kt & 3) == 0 && gi + 1 < ngroups) group_load(cur, (gi + 1 + gpar) & 1, gi + 1);
+            TileState ld;   // field by field: a selected reference would live in scratch memory
+            ld.a.e = last ? nxt.a.e : cur.a.e;
+            ld.a.o = last ? nxt.a.o : cur.a.o;
+            ld.b.e = last ? nxt.b.e : cur.b.e;
+            ld.b.o = last ? nxt.b.o : cur.b.o;
+            ld.sa_row = last ? nxt.sa_row : cur.sa_row;
+            ld.sb_row = last ? nxt.sb_row : cur.sb_row;
+            const uint32_t ko = last ? 0u : (uint32_t)(kt + 1) * BK;
+            const uint8_t* la = lds_all + ((kt + par) & 1) * kStage;
+            const uint8_t* lb = la + kTileBytes;
+            uint8_t* dst = lds_all + ((kt + 1 + par) & 1) * kStage;
+            v8i b[4], a[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = frag2(lb, wn + 16 * j);
+            a[0] = frag2(la, wm);
+            a[1] = frag2(la, wm + 16);
+#pragma unroll
+            for (int u = 0; u < 12; ++u) stage_load(ld, ko, dst, u);
+            float sbc = 0.f;
+            if constexpr (!BROW) {
+                sbc = sbn;
+                sbn = load_f32(rsb, ld.sb_row + (last ? 0u : (uint32_t)(kt + 1) * ksb4));
+            }
+            // this step's scales: A rows of the lane's 8 fragment rows; B rows
+            // of its 4 x 4 columns (row scales) or the wave's block scale
+            const uint8_t* gs = lds_sc + ((gi + gpar) & 1) * kScGroup + 4 * (kt & 3);
+            float sf[8], sbr[NSB];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float sa = *reinterpret_cast<const float*>(gs + (wm + 16 * i + (l & 15)) * 16);
+                sf[i] = BROW ? sa : sa * sbc;
+            }
+            if constexpr (BROW) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    sbr[q] = *reinterpret_cast<const float*>(gs + kScA + (wn + 16 * (q >> 2) + 4 * (l >> 4) + (q & 3)) * 16);
+            }
+            row_fma(7, sf7, sb7);
+            // fragment row i + 1's MFMAs run while row i's partials are added;
+            // row i + 2's fragment is read into the registers row i used
+            auto row_mfma = [&](int i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    p[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        b[j], a[i & 1], v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA, 0, 0, 0, 0);
+            };
+            row_mfma(0);
+#pragma unroll
+            for (int i = 0; i < 7; ++i) {
+                row_mfma(i + 1);
+                if (i + 2 < 8) a[i & 1] = frag2(la, wm + 16 * (i + 2));
+                row_fma(i, sf[i], sbr);
+            }
+            sf7 = sf[7];
+#pragma unroll
+            for (int q = 0; q < NSB; ++q) sb7[q] = sbr[q];
+            lds_wait_all();
+        }
+        row_fma(7, sf7, sb7);
+        // every wave is done reading the last stage before it is reused
+        stage_barrier();
+
+        int tm, tn;
+        tile_coords(logical, ntm, ntn, tm, tn);
+        const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNb;
+        uint8_t* ep0 = lds_all + ((nk - 1 + par) & 1) * kStage;
+        if constexpr (OUT == FP8Q_BF16) {
+            typedef float v2f_t __attribute__((ext_vector_type(2)));
+            typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+            constexpr int kPitch = 144;   // 64 bf16 + 16 bytes
+            uint8_t* ep = ep0 + w * (32 * kPitch);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const v4f v = acc[2 * qq + ii][j];
+                        const v2bf_t p0 = __builtin_convertvector(v2f_t{v[0], v[1]}, v2bf_t);
+                        const v2bf_t p1 = __builtin_convertvector(v2f_t{v[2], v[3]}, v2bf_t);
+                        const int row = 16 * ii + (l & 15);
+                        *reinterpret_cast<uint2*>(ep + row * kPitch + (16 * j + 4 * (l >> 4)) * 2) =
+                            make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+                    }
+                lds_wait_all();
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int row = 8 * u + (l >> 3), ch = l & 7;
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kPitch + ch * 16);
+                    const int64_t m = m0 + wm + 32 * qq + row;
+                    const int64_t n = n0 + wn + ch * 8;
+                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n) = d;
+                }
+            }
+        } else {
+            constexpr int kPitch = 272;   // 64 fp32 + 16 bytes
+            uint8_t* ep = ep0 + w * (16 * kPitch);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<v4f*>(ep + (l & 15) * kPitch + (16 * j + 4 * (l >> 4)) * 4) = acc[i][j];
+                lds_wait_all();
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int row = 4 * u + (l >> 4), ch = l & 15;
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kPitch + ch * 16);
+                    const int64_t m = m0 + wm + 16 * i + row;
+                    const int64_t n = n0 + wn + ch * 4;
+                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(g.C) + m * N + n) = d;
+                }
+            }
+        }
+        if (!has_next) break;
+        logical = next;
+        par = (nk + par) & 1;
+        gpar = (ngroups + gpar) & 1;
+        cur = nxt;
+    }
+    // the last step's extra loads land before the workgroup's LDS is released
+    vm_wait<0>();
+}
+
+
+template <int FA, int FB, int OUT>
+static void launch_out(const GemmArgs& g, hipStream_t s) {
+    const int ntm = (int)((g.M + BM - 1) / BM), ntn = (int)((g.N + 127) / 128);
+    if (g.sb.rshift == 0)
+        hipLaunchKernelGGL((gemm_bs_kernel<FA, FB, OUT, true>), dim3(persistent_grid()), dim3(kThreads), 0, s, g, ntm,
+                           ntn);
+    else
+        hipLaunchKernelGGL((gemm_bs_kernel<FA, FB, OUT, false>), dim3(persistent_grid()), dim3(kThreads), 0, s, g,
+                           ntm, ntn);
+}
+
+template <int FA, int FB>
+static void launch_fb(const GemmArgs& g, hipStream_t s) {
+    if (g.c_dtype == FP8Q_BF16) launch_out<FA, FB, FP8Q_BF16>(g, s);
+    else launch_out<FA, FB, FP8Q_F32>(g, s);
+}
+
+bool launch_gemm_block_persistent(const GemmArgs& g, hipStream_t s) {
+    // direct-to-LDS operand loads: K a multiple of the 128-K step, at least
+    // two steps, every lane offset below 2^32; row scales staged in groups of
+    // four K blocks (16 bytes per row): K % 512 == 0, K-contiguous, 16-byte
+    // aligned rows; B either row scales or 128x128 blocks
+    auto rows16 = [](const GemmScale& sc) {
+        return sc.rshift == 0 && sc.kstride == 1 && sc.ld % 4 == 0 && (uintptr_t)sc.s % 16 == 0;
+    };
+    const bool offsets32 = g.M * g.K < (int64_t(1) << 32) && g.N * g.K < (int64_t(1) << 32);
+    const bool scales32 = g.M * (g.K / BK) < (int64_t(1) << 29) && g.N * (g.K / BK) < (int64_t(1) << 29);
+    if (!(g.K % 512 == 0 && g.K >= 2 * BK && offsets32 && scales32 && rows16(g.sa))) return false;
+    if (!(rows16(g.sb) || g.sb.rshift == 7)) return false;
+    if (g.fa == FP8Q_E4M3) {
+        if (g.fb == FP8Q_E4M3) launch_fb<FP8Q_E4M3, FP8Q_E4M3>(g, s);
+        else launch_fb<FP8Q_E4M3, FP8Q_E5M2>(g, s);
+    } else {
+        if (g.fb == FP8Q_E4M3) launch_fb<FP8Q_E5M2, FP8Q_E4M3>(g, s);
+        else launch_fb<FP8Q_E5M2, FP8Q_E5M2>(g, s);
+    }
+    return true;
+}
+
+}  // namespace fp8q

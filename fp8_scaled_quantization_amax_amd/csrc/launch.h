@@ -90,5 +90,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+// Block-scaled GEMM on the persistent kernel when its conditions hold (K %
+// 512 == 0, K-contiguous 16-byte-aligned row scales, ...); false: not launched.
+bool launch_gemm_block_persistent(const GemmArgs& g, hipStream_t s);
 
 }  // namespace fp8q

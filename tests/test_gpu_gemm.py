@@ -159,8 +159,12 @@ def block_operands(op, M, N, K, seed):
     return A, B
 
 
+# K = 128 or K % 512 != 0: the register-staged kernel; K % 512 == 0 (8, 4 and
+# 12 K steps, ragged M and N): the persistent block-scaled kernel, with one
+# scale per wave for 128x128-block B (NT, NN) and per-row B scales (TN).
 @pytest.mark.parametrize("op", ["NT", "NN", "TN"])
-@pytest.mark.parametrize("shape", [(256, 128, 128), (528, 400, 640), (1024, 1536, 1024)])
+@pytest.mark.parametrize("shape", [(256, 128, 128), (528, 400, 640), (1024, 1536, 1024), (1040, 784, 512),
+                                   (784, 1040, 1536)])
 def test_block_scaled(op, shape):
     M, N, K = shape
     announce("gemm block-scaled", op, shape)
@@ -187,6 +191,41 @@ def test_block_scaled(op, shape):
     # autocast with the same granularities gives the same result
     Ca = GEMM[op](M, N, K, AC(A.to(dev()), fa, fq.TILE_1x128), AC(B.to(dev()), fb, gb), torch.float32)
     assert gemm_close(Ca, ref, torch.float32)
+
+
+def block_scaled_codes(op, A, B, fa, fb):
+    """Device codes and oracle codes / scales of a block-scaled GEMM's operands."""
+    axis_a = 0 if kcontig(op, "A") else 1
+    qa, qaT, sa = fq.fp8_quantize_tile1x128(A.to(dev()), axis_a, fa, emit_t=not kcontig(op, "A"))
+    oqa, osa = oracle.quantize_tiles(host_input(A), axis_a, 128, fa)
+    if op == "TN":
+        qb, qbT, sb = fq.fp8_quantize_tile1x128(B.to(dev()), 1, fb, emit_t=True)
+        oqb, osb = oracle.quantize_tiles(host_input(B), 1, 128, fb)
+        gb, oscale_b = fq.TILE_1x128, oracle.Scale("rowk", osb, kblk=128)
+    else:
+        qb, qbT, sb = fq.fp8_quantize_block128x128(B.to(dev()), fb, emit_t=not kcontig(op, "B"))
+        oqb, osb = oracle.quantize_blocks(host_input(B), 128, 128, fb)
+        gb = fq.BLOCK_128x128
+        oscale_b = oracle.Scale("block" if op == "NT" else "blockT", osb, kblk=128, rblk=128)
+    oa = Q(qa, fa, sa, fq.TILE_1x128, kmajor=qaT)
+    ob = Q(qb, fb, sb, gb, kmajor=qbT)
+    return oa, ob, oqa, oqb, oracle.Scale("rowk", osa, kblk=128), oscale_b
+
+
+@pytest.mark.parametrize("op", ["NT", "NN", "TN"])
+def test_block_scaled_persistent_multi_tile(op):
+    """Block-scaled with more output tiles than workgroups, an odd number of
+    four-step scale groups and bf16 output: sampled rows (tile edges
+    included) against the oracle."""
+    M, N, K = 4112, 4112, 1536
+    announce("gemm block-scaled multi-tile", op)
+    A, B = block_operands(op, M, N, K, seed=250)
+    fa, fb = (fq.E5M2, fq.E4M3) if op != "NT" else (fq.E4M3, fq.E4M3)
+    oa, ob, oqa, oqb, osa, osb = block_scaled_codes(op, A, B, fa, fb)
+    rows = sample_rows(M, seed=M + K + 2)
+    ref = OGEMM[op](oqa, oqb, fa, fb, osa, osb, rows=rows)
+    C = GEMM[op](M, N, K, oa, ob, torch.bfloat16)
+    assert gemm_close(C[torch.as_tensor(rows, device=C.device)], ref, torch.bfloat16)
 
 
 # K = 128 or K % 128 != 0: the register-staged kernel; K >= 256 with K % 128 == 0

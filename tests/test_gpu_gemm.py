@@ -321,3 +321,35 @@ def test_full_layer_gemm_sampled(gemm):
         oqb = np.ascontiguousarray(oqb.T)
     ref = oracle.gemm_nt(oqa, oqb, fa, fq.E4M3, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb), rows=rows)
     assert gemm_close(C[torch.from_numpy(rows).to(dev())], ref, torch.bfloat16)
+
+
+def mx_codes(op, A, B, fa, fb):
+    """Device codes and oracle codes / exponents of an MX32 GEMM's operands."""
+    axa = 0 if kcontig(op, "A") else 1
+    axb = 0 if kcontig(op, "B") else 1
+    qa, qaT, ea = fq.fp8_quantize_mx32(A.to(dev()), axa, fa, emit_t=axa == 1)
+    qb, qbT, eb = fq.fp8_quantize_mx32(B.to(dev()), axb, fb, emit_t=axb == 1)
+    oqa, oea = oracle.quantize_tiles(host_input(A), axa, 32, fa, mx=True)
+    oqb, oeb = oracle.quantize_tiles(host_input(B), axb, 32, fb, mx=True)
+    return (Q(qa, fa, ea, fq.MX32, kmajor=qaT), Q(qb, fb, eb, fq.MX32, kmajor=qbT), oqa, oqb,
+            oracle.Scale("rowk", oea, kblk=32, e8m0=True), oracle.Scale("rowk", oeb, kblk=32, e8m0=True))
+
+
+@pytest.mark.parametrize("recipe", ["block", "mx"])
+@pytest.mark.parametrize("gemm", [g for g in workloads.layer_gemms() if g[0].startswith("attn_out")],
+                         ids=lambda g: g[0])
+def test_full_attn_out_granular_sampled(gemm, recipe):
+    """The attention-output GEMMs at full size in the benchmark's block-scaled
+    and MX32 recipes (N(0,1) operands with 1% of rows x1e3; fprop E4M3 x E4M3,
+    dgrad / wgrad E5M2 x E4M3; bf16 out), on sampled output rows."""
+    name, op, M, N, K = gemm
+    announce("full granular", recipe, name, op, M, N, K)
+    A, B = workloads.gemm_operands(op, M, N, K, seed=7000 + zlib.crc32(name.encode()) % 1000, std=1.0,
+                                   outlier_rows=0.01, device=dev())
+    fa, fb = (fq.E4M3, fq.E4M3) if op == "NT" else (fq.E5M2, fq.E4M3)
+    codes = block_scaled_codes if recipe == "block" else mx_codes
+    oa, ob, oqa, oqb, osa, osb = codes(op, A, B, fa, fb)
+    rows = sample_rows(M, 3, n_tiles=3, n_rand=4)
+    ref = OGEMM[op](oqa, oqb, fa, fb, osa, osb, rows=rows)
+    C = GEMM[op](M, N, K, oa, ob, torch.bfloat16)
+    assert gemm_close(C[torch.as_tensor(rows, device=C.device)], ref, torch.bfloat16)

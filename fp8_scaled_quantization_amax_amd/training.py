@@ -1,0 +1,83 @@
+"""Simulated-FP8 training on the library's kernels.
+
+`FP8Matmul` is y = x . w^T with both GEMM inputs quantized to E4M3 in the
+forward and the output gradient quantized to E5M2 in the backward, each with
+its per-tensor current scale.  Accumulation and outputs stay fp32, and the
+fp32 master weights the optimizer updates are never stored in FP8.  It
+follows the "fp8_parity.py" lab page: the class FP8Matmul and the small-MLP
+training of its smoke check [5].
+
+How the library is used:
+
+- The forward quantizes x and w with their transposed copies.
+- It saves the codes, so the backward reuses the forward's E4M3 operands, as
+  the page saves `xq` and `wq`.
+- fprop is the NT GEMM, dgrad = E5M2(dy) . E4M3(w) is the NN GEMM, and
+  wgrad = E5M2(dy)^T . E4M3(x) is the TN GEMM.
+
+Every quantize and GEMM runs in libfp8q's HIP kernels.  The MLP's relu, tanh
+targets, loss and AdamW are plain torch ops around them.
+"""
+import torch
+
+from . import (E4M3, E5M2, GemmOperand, fp8_gemm_scaled_NN, fp8_gemm_scaled_NT, fp8_gemm_scaled_TN,
+               fp8_quantize_per_tensor)
+
+
+class FP8Matmul(torch.autograd.Function):
+    """y[M,N] = x[M,K] . w[N,K]^T in FP8 (E4M3 forward, E5M2 output gradient)."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+            raise ValueError(f"FP8Matmul needs x[M,K] and w[N,K], got {tuple(x.shape)} and {tuple(w.shape)}")
+        x, w = x.contiguous(), w.contiguous()
+        M, K = x.shape
+        N = w.shape[0]
+        qx, qxT, sx, _ = fp8_quantize_per_tensor(x, E4M3, emit_t=True)
+        qw, qwT, sw, _ = fp8_quantize_per_tensor(w, E4M3, emit_t=True)
+        y = fp8_gemm_scaled_NT(M, N, K, GemmOperand.quantized(qx, E4M3, sx),
+                               GemmOperand.quantized(qw, E4M3, sw), torch.float32)
+        ctx.save_for_backward(qx, qxT, sx, qw, qwT, sw)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        qx, qxT, sx, qw, qwT, sw = ctx.saved_tensors
+        dy = dy.contiguous()
+        M, N = dy.shape
+        K = qx.shape[1]
+        qg, qgT, sg, _ = fp8_quantize_per_tensor(dy, E5M2, emit_t=True)
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            dx = fp8_gemm_scaled_NN(M, K, N, GemmOperand.quantized(qg, E5M2, sg),
+                                    GemmOperand.quantized(qw, E4M3, sw, kmajor=qwT), torch.float32)
+        if ctx.needs_input_grad[1]:
+            dw = fp8_gemm_scaled_TN(N, K, M, GemmOperand.quantized(qg, E5M2, sg, kmajor=qgT),
+                                    GemmOperand.quantized(qx, E4M3, sx, kmajor=qxT), torch.float32)
+        return dx, dw
+
+
+def fp8_matmul(x, w):
+    """x . w^T through FP8Matmul."""
+    return FP8Matmul.apply(x, w)
+
+
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3):
+    """The lab page's check-[5] loop: the 2-layer MLP relu(X W1^T) W2^T is fitted
+    to Y by mean squared error with AdamW(lr), with every matmul either FP8
+    (`fp8_matmul`) or plain fp32.  X, Y, W1 and W2 are device tensors; the
+    weights are copied and left unchanged.  Returns the list of per-step
+    losses (floats, read once at the end)."""
+    W1 = W1.detach().clone().requires_grad_()
+    W2 = W2.detach().clone().requires_grad_()
+    opt = torch.optim.AdamW([W1, W2], lr=lr)
+    mm = fp8_matmul if fp8 else (lambda a, b: a @ b.T)
+    losses = []
+    for _ in range(steps):
+        loss = ((mm(torch.relu(mm(X, W1)), W2) - Y) ** 2).mean()
+        opt.zero_grad()
+        loss.backward()
+        opt.step()
+        losses.append(loss.detach())
+    return [float(v) for v in torch.stack(losses).cpu()]

@@ -1,0 +1,60 @@
+"""Oracle side of simulated-FP8 training (the "fp8_parity.py" lab page, class
+FP8Matmul and smoke check [5]).
+
+TEST INFRASTRUCTURE ONLY, like the rest of oracle/.  `OracleFP8Matmul` is the
+page's FP8Matmul written on the oracle's own definitions:
+
+- each GEMM input is quantized with the oracle's per-tensor current scaling
+  (E4M3 for x and w, E5M2 for the output gradient);
+- the product is the oracle's exact integer GEMM, scaled in fp64 and then
+  rounded once to fp32.
+
+The page multiplies dequantized fp32 tensors (xq @ wq.T).  That is the same
+product up to fp32 summation order.  `train_mlp` is the page's check-[5]
+loop on the CPU.
+"""
+import numpy as np
+import torch
+
+from . import E4M3, E5M2, Scale, gemm_nn, gemm_nt, gemm_tn, quantize_per_tensor
+
+
+def _q(t, fmt):
+    q, s, _ = quantize_per_tensor(t.detach().contiguous().numpy(), fmt)
+    return q, Scale("tensor", s)
+
+
+class OracleFP8Matmul(torch.autograd.Function):
+    """y = x . w^T with E4M3 inputs forward and an E5M2 output gradient backward."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        qx, sx = _q(x, E4M3)
+        qw, sw = _q(w, E4M3)
+        ctx.saved = (qx, sx, qw, sw)
+        return torch.from_numpy(gemm_nt(qx, qw, E4M3, E4M3, sx, sw).astype(np.float32))
+
+    @staticmethod
+    def backward(ctx, dy):
+        qx, sx, qw, sw = ctx.saved
+        qg, sg = _q(dy, E5M2)
+        dx = torch.from_numpy(gemm_nn(qg, qw, E5M2, E4M3, sg, sw).astype(np.float32))
+        dw = torch.from_numpy(gemm_tn(qg, qx, E5M2, E4M3, sg, sx).astype(np.float32))
+        return dx, dw
+
+
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3):
+    """Fit relu(X W1^T) W2^T to Y by mean squared error with AdamW(lr), every
+    matmul either OracleFP8Matmul or plain fp32; returns the per-step losses."""
+    W1 = W1.detach().clone().requires_grad_()
+    W2 = W2.detach().clone().requires_grad_()
+    opt = torch.optim.AdamW([W1, W2], lr=lr)
+    mm = OracleFP8Matmul.apply if fp8 else (lambda a, b: a @ b.T)
+    losses = []
+    for _ in range(steps):
+        loss = ((mm(torch.relu(mm(X, W1)), W2) - Y) ** 2).mean()
+        opt.zero_grad()
+        loss.backward()
+        opt.step()
+        losses.append(loss.item())
+    return losses

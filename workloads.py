@@ -12,6 +12,8 @@ follow a transformer layer with hidden 4096, FFN 16384, M = 31 x 512 tokens):
                  delayed-scaling steps with a 40-sigma spike (0.625) on the last step
   layer GEMMs    12 fprop/dgrad/wgrad GEMMs, operands ~ N(0,1)/sqrt(K) bf16
   block-scaled   the same shapes, operands ~ N(0,1) bf16 with 1% rows x1e3
+  lab MLP        the training-parity draws of the lab page (X[512,32], teacher
+                 targets Y = tanh(X . W^T) in plain fp32, W1[64,32]/6, W2[16,64]/8)
 Outliers and spikes are applied to the bf16-rounded tensor in fp32 and the
 result is rounded to bf16 again.
 """
@@ -153,3 +155,18 @@ def lab_smoke_inputs():
     a = torch.randn(8, 128) * 0.01
     a[0] *= 1e4
     return {"x": x, "big": big, "history": history, "act": act, "a": a}
+
+
+def lab_mlp_inputs():
+    """The draws of the same page's check [5] (small-MLP training): after the
+    draws of checks [1]-[4], X = randn(512, 32) and a teacher weight
+    randn(16, 32) / 6 giving targets Y = tanh(X . W^T); then, under
+    torch.manual_seed(1), the initial weights W1 = randn(64, 32) / 6 and
+    W2 = randn(16, 64) / 8.  fp32 CPU tensors."""
+    lab_smoke_inputs()
+    X = torch.randn(512, 32)
+    Y = torch.tanh(X @ (torch.randn(16, 32) / 6).T)
+    torch.manual_seed(1)
+    W1 = torch.randn(64, 32) / 6
+    W2 = torch.randn(16, 64) / 8
+    return {"X": X, "Y": Y, "W1": W1, "W2": W2}

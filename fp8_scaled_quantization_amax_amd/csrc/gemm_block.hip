@@ -195,20 +195,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                     sbr[q] = *reinterpret_cast<const float*>(gs + kScA + (wn + 16 * (q >> 2) + 4 * (l >> 4) + (q & 3)) * 16);
             }
             row_fma(7, sf7, sb7);
-            // fragment row i + 1's MFMAs run while row i's partials are added;
-            // row i + 2's fragment is read into the registers row i used
-            auto row_mfma = [&](int i) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    p[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        b[j], a[i & 1], v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA, 0, 0, 0, 0);
+            // Fragment row i + 1's MFMAs run while row i's partials are added:
+            // MFMA (i + 1, j), then the four FMAs of (i, j), whose partial was
+            // produced four MFMAs earlier.  Row i + 2's fragment is read into
+            // the registers row i used.  The scheduling barriers keep this
+            // order (left free, the compiler put each FMA group right behind
+            // the MFMA producing it and waited for that MFMA with s_nops).
+            auto mfma_one = [&](int i, int j) {
+                p[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    b[j], a[i & 1], v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA, 0, 0, 0, 0);
             };
-            row_mfma(0);
+            auto fma_one = [&](int i, int j, float sv, const float* sb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] = __builtin_fmaf(p[i & 1][j][r], BROW ? sv * sb[4 * j + r] : sv, acc[i][j][r]);
+            };
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mfma_one(0, j);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 7; ++i) {
-                row_mfma(i + 1);
-                if (i + 2 < 8) a[i & 1] = frag2(la, wm + 16 * (i + 2));
-                row_fma(i, sf[i], sbr);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    mfma_one(i + 1, j);
+                    if (j == 0 && i + 2 < 8) a[i & 1] = frag2(la, wm + 16 * (i + 2));
+                    fma_one(i, j, sf[i], sbr);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             sf7 = sf[7];
 #pragma unroll

@@ -25,36 +25,44 @@ from . import (E4M3, E5M2, GemmOperand, fp8_gemm_scaled_NN, fp8_gemm_scaled_NT, 
 
 
 class FP8Matmul(torch.autograd.Function):
-    """y[M,N] = x[M,K] . w[N,K]^T in FP8 (E4M3 forward, E5M2 output gradient)."""
+    """y[M,N] = x[M,K] . w[N,K]^T in FP8 (E4M3 forward, E5M2 output gradient).
+
+    x and w are fp32 or bf16 (the same dtype); y, dx and dw come out in that
+    dtype (fp32 accumulation, one rounding at the end)."""
 
     @staticmethod
     def forward(ctx, x, w):
         if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
             raise ValueError(f"FP8Matmul needs x[M,K] and w[N,K], got {tuple(x.shape)} and {tuple(w.shape)}")
+        if x.dtype != w.dtype or x.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"FP8Matmul needs x and w both fp32 or both bf16, got {x.dtype} and {w.dtype}")
         x, w = x.contiguous(), w.contiguous()
         M, K = x.shape
         N = w.shape[0]
-        qx, qxT, sx, _ = fp8_quantize_per_tensor(x, E4M3, emit_t=True)
-        qw, qwT, sw, _ = fp8_quantize_per_tensor(w, E4M3, emit_t=True)
+        # K-major copies only for the backward GEMMs that will run: x's for
+        # wgrad, w's for dgrad (none in forward-only use)
+        qx, qxT, sx, _ = fp8_quantize_per_tensor(x, E4M3, emit_t=ctx.needs_input_grad[1])
+        qw, qwT, sw, _ = fp8_quantize_per_tensor(w, E4M3, emit_t=ctx.needs_input_grad[0])
         y = fp8_gemm_scaled_NT(M, N, K, GemmOperand.quantized(qx, E4M3, sx),
-                               GemmOperand.quantized(qw, E4M3, sw), torch.float32)
+                               GemmOperand.quantized(qw, E4M3, sw), x.dtype)
         ctx.save_for_backward(qx, qxT, sx, qw, qwT, sw)
+        ctx.dtype = x.dtype
         return y
 
     @staticmethod
     def backward(ctx, dy):
         qx, qxT, sx, qw, qwT, sw = ctx.saved_tensors
-        dy = dy.contiguous()
+        dy = dy.to(ctx.dtype).contiguous()
         M, N = dy.shape
         K = qx.shape[1]
         qg, qgT, sg, _ = fp8_quantize_per_tensor(dy, E5M2, emit_t=True)
         dx = dw = None
         if ctx.needs_input_grad[0]:
             dx = fp8_gemm_scaled_NN(M, K, N, GemmOperand.quantized(qg, E5M2, sg),
-                                    GemmOperand.quantized(qw, E4M3, sw, kmajor=qwT), torch.float32)
+                                    GemmOperand.quantized(qw, E4M3, sw, kmajor=qwT), ctx.dtype)
         if ctx.needs_input_grad[1]:
             dw = fp8_gemm_scaled_TN(N, K, M, GemmOperand.quantized(qg, E5M2, sg, kmajor=qgT),
-                                    GemmOperand.quantized(qx, E4M3, sx, kmajor=qxT), torch.float32)
+                                    GemmOperand.quantized(qx, E4M3, sx, kmajor=qxT), ctx.dtype)
         return dx, dw
 
 

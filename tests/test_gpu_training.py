@@ -90,3 +90,31 @@ def test_lab_check5_training_parity(training, lab):
     # claim.  (Measured on MI355X: 1.7e-5 at step 0, 3e-4 over the first 10
     # steps, 1.1e-2 over all 300.)
     assert rel.max() < 0.05
+
+
+def test_fp8_matmul_bf16_matches_oracle(training, lab):
+    """bf16 activations and weights: the quantizer widens them exactly, so the
+    codes are the oracle's on the fp32 copies; y, dx, dw come out in bf16 and
+    agree within max |diff| <= 2^-7 max |oracle|."""
+    dev = torch.device("cuda")
+    h = torch.relu(lab["X"] @ lab["W1"].T).to(torch.bfloat16)
+    w = lab["W2"].to(torch.bfloat16)
+    g = (torch.randn(512, 16, generator=torch.Generator().manual_seed(6)) * 1e-3).to(torch.bfloat16)
+    xo, wo = h.float().requires_grad_(), w.float().requires_grad_()
+    yo = fp8_train.OracleFP8Matmul.apply(xo, wo)
+    yo.backward(g.float())
+    xg, wg = h.to(dev).requires_grad_(), w.to(dev).requires_grad_()
+    yg = training.FP8Matmul.apply(xg, wg)
+    yg.backward(g.to(dev))
+    torch.cuda.synchronize()
+    for got, ref, what in ((yg, yo, "y"), (xg.grad, xo.grad, "dx"), (wg.grad, wo.grad, "dw")):
+        assert got.dtype == torch.bfloat16, what
+        got, ref = got.detach().double().cpu(), ref.detach().double()
+        err = (got - ref).abs().max().item()
+        assert err <= 2.0 ** -7 * ref.abs().max().item(), f"{what}: {err}"
+
+
+def test_fp8_matmul_rejects_mixed_dtypes(training):
+    dev = torch.device("cuda")
+    with pytest.raises(ValueError):
+        training.FP8Matmul.apply(torch.zeros(32, 16, device=dev), torch.zeros(16, 16, device=dev, dtype=torch.bfloat16))

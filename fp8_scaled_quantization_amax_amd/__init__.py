@@ -13,7 +13,7 @@ import torch
 
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
-PER_TENSOR, TILE_1x128, BLOCK_128x128, MX32 = 0, 1, 2, 3
+PER_TENSOR, TILE_1x128, BLOCK_128x128, MX32, ROWWISE = 0, 1, 2, 3, 4
 CURRENT, DELAYED = 0, 1
 SATURATE = 1
 HISTORY_LEN = 16
@@ -64,6 +64,7 @@ def lib():
             "fp8_quantize_tile1x128": (I, [P, I, I64, I64, I, I, P, P, P, U, P]),
             "fp8_quantize_block128x128": (I, [P, I, I64, I64, I, P, P, P, U, P]),
             "fp8_quantize_mx32": (I, [P, I, I64, I64, I, I, P, P, P, U, P]),
+            "fp8_quantize_rowwise": (I, [P, I, I64, I64, I, I, P, P, P, U, P]),
             "fp8_gemm_workspace_bytes": (SZ, [I, I64, I64, I64, OP, OP]),
             "fp8_gemm_scaled_NT": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
             "fp8_gemm_scaled_NN": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
@@ -204,6 +205,21 @@ def fp8_quantize_mx32(x, axis=0, fmt=E4M3, emit_t=False, saturate=False):
     _check(lib().fp8_quantize_mx32(_ptr(x), hp, rows, cols, axis, fmt, _ptr(q), _ptr(qT), _ptr(e8),
                                    SATURATE if saturate else 0, _stream()))
     return q, qT, e8
+
+
+def fp8_quantize_rowwise(x, axis=0, fmt=E4M3, emit_t=False, saturate=False):
+    """One scale per row (axis 0) or per column (axis 1); returns (q, qT, scales).
+    qT (the K-major copy) is available with axis 1 only."""
+    hp = _hp(x)
+    rows, cols = _rows_cols(x)
+    if emit_t and axis == 0:
+        raise ValueError("rowwise axis 0 has no transposed copy")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if emit_t else None
+    sc = torch.empty(rows if axis == 0 else cols, dtype=torch.float32, device=x.device)
+    _check(lib().fp8_quantize_rowwise(_ptr(x), hp, rows, cols, axis, fmt, _ptr(q), _ptr(qT), _ptr(sc),
+                                      SATURATE if saturate else 0, _stream()))
+    return q, qT, sc
 
 
 # ---------------------------------------------------------------- GEMM

@@ -103,7 +103,10 @@ int validate_operand(const fp8q_operand* o, const char* name, int64_t K) {
     if (o->data == nullptr) return fail(FP8Q_EINVAL, "operand %s has no data", name);
     if (!valid_fmt(o->format)) return fail(FP8Q_EINVAL, "operand %s: unknown format %d", name, o->format);
     const int gr = o->granularity;
-    if (gr < FP8Q_PER_TENSOR || gr > FP8Q_MX32) return fail(FP8Q_EINVAL, "operand %s: unknown granularity %d", name, gr);
+    if (gr < FP8Q_PER_TENSOR || gr > FP8Q_ROWWISE)
+        return fail(FP8Q_EINVAL, "operand %s: unknown granularity %d", name, gr);
+    if (gr == FP8Q_ROWWISE && !o->quantized)
+        return fail(FP8Q_EUNSUPPORTED, "operand %s: rowwise scaling needs pre-quantized codes (no autocast)", name);
     if ((gr == FP8Q_TILE_1x128 || gr == FP8Q_BLOCK_128x128) && K % 128 != 0)
         return fail(FP8Q_EALIGN, "operand %s: K=%lld must be a multiple of 128 for 1x128 / 128x128 scaling", name,
                     (long long)K);
@@ -132,6 +135,7 @@ size_t scale_bytes_for(int gran, int64_t R, int64_t K) {
         case FP8Q_PER_TENSOR: return sizeof(float);
         case FP8Q_TILE_1x128: return (size_t)R * (size_t)(K / 128) * sizeof(float);
         case FP8Q_BLOCK_128x128: return (size_t)((R + 127) / 128) * (size_t)(K / 128) * sizeof(float);
+        case FP8Q_ROWWISE: return (size_t)R * sizeof(float);
         default: return (size_t)R * (size_t)(K / 32);
     }
 }
@@ -146,6 +150,9 @@ int plan_gemm(int op, int64_t M, int64_t N, int64_t K, const fp8q_operand* A, co
     if ((r = validate_operand(B, "B", K)) != FP8Q_OK) return r;
     const bool amx = A->granularity == FP8Q_MX32, bmx = B->granularity == FP8Q_MX32;
     if (amx != bmx) return fail(FP8Q_EUNSUPPORTED, "MX32 scaling must be used on both operands");
+    const bool arow = A->granularity == FP8Q_ROWWISE, brow = B->granularity == FP8Q_ROWWISE;
+    if ((arow || brow) && !((arow || A->granularity == FP8Q_PER_TENSOR) && (brow || B->granularity == FP8Q_PER_TENSOR)))
+        return fail(FP8Q_EUNSUPPORTED, "rowwise scaling combines only with rowwise or per-tensor scaling");
     size_t off = 0;
     p.partials_off = 0;
     bool need_partials = false;
@@ -185,6 +192,7 @@ fp8q::GemmScale make_scale(int gran, const void* s, bool kcontig_stored, int64_t
     switch (gran) {
         case FP8Q_PER_TENSOR: break;
         case FP8Q_TILE_1x128: g.ld = K / 128; g.kstride = 1; g.rshift = 0; break;
+        case FP8Q_ROWWISE: g.ld = 1; g.kstride = 0; g.rshift = 0; break;
         case FP8Q_BLOCK_128x128:
             g.rshift = 7;
             if (kcontig_stored) { g.ld = K / 128; g.kstride = 1; }
@@ -404,6 +412,23 @@ int fp8_quantize_tile1x128(const void* x, int hp, int64_t rows, int64_t cols, in
     a.q = q; a.qT = qT; a.scales = scales;
     a.scheme = axis == 0 ? fp8q::kTileAxis0 : fp8q::kTileAxis1;
     if ((r = launched(fp8q::launch_quantize(a, reinterpret_cast<hipStream_t>(stream)), "quantize")) != FP8Q_OK)
+        return r;
+    return ok();
+}
+
+int fp8_quantize_rowwise(const void* x, int hp, int64_t rows, int64_t cols, int axis, int fmt, uint8_t* q,
+                         uint8_t* qT, float* scales, unsigned flags, void* stream) {
+    int r;
+    if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags)) != FP8Q_OK) return r;
+    if (scales == nullptr) return fail(FP8Q_EINVAL, "scales is required");
+    if (axis != 0 && axis != 1) return fail(FP8Q_EINVAL, "axis must be 0 or 1");
+    if (axis == 0 && qT != nullptr)
+        return fail(FP8Q_EUNSUPPORTED, "rowwise axis 0 writes no transposed copy (qT must be NULL)");
+    if ((uintptr_t)scales % sizeof(float) != 0) return fail(FP8Q_EALIGN, "scales is not 4-byte aligned");
+    if ((r = check_device()) != FP8Q_OK) return r;
+    if ((r = launched(fp8q::launch_quantize_rowwise(x, hp, rows, cols, axis, fmt, (flags & FP8Q_SATURATE) != 0, q, qT,
+                                                    scales, reinterpret_cast<hipStream_t>(stream)),
+                      "quantize")) != FP8Q_OK)
         return r;
     return ok();
 }

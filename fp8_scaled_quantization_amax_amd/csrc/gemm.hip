@@ -41,7 +41,9 @@
 namespace fp8q {
 
 
-enum ScaleMode : int { kSmPerTensor = 0, kSmBlock = 1, kSmMx = 2 };
+// kSmRow: one scale per operand row (rowwise recipe; a per-tensor operand
+// broadcasts its scale), applied in the epilogue as acc * (sA[m] * sB[n]).
+enum ScaleMode : int { kSmPerTensor = 0, kSmBlock = 1, kSmMx = 2, kSmRow = 3 };
 
 // Logical tile of this workgroup: XCD-contiguous, then grouped by 8 M-tiles.
 __device__ __forceinline__ void tile_of_block(int ntm, int ntn, int& tm, int& tn) {
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, int ntm, 
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bf[j] = frag(lb, wn + 16 * j);
 
-        if constexpr (SM == kSmPerTensor) {
+        if constexpr (SM == kSmPerTensor || SM == kSmRow) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const v8i af = frag(la, wm + 16 * i);
@@ -257,7 +259,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, int ntm, 
         for (int j = 0; j < NJ; ++j) {
             const int64_t n = n0 + wn + 16 * j + 4 * (l >> 4);
             if (n >= N) continue;
-            const v4f v = acc[i][j] * S;
+            v4f v = acc[i][j] * S;
+            if constexpr (SM == kSmRow) {
+                const float sam = row_scale(g.sa, m, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * (sam * row_scale(g.sb, n + r, 0));
+            }
             if constexpr (OUT == FP8Q_BF16) {
                 const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
                 const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
@@ -386,6 +393,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
         load_group(0, sa_off, sb_off, 0);
     }
     const float S = MX ? 1.0f : reinterpret_cast<const float*>(g.sa.s)[0] * reinterpret_cast<const float*>(g.sb.s)[0];
+    // kSmRow: this lane's scales of its 8 output rows (16 i + l % 16 of the
+    // wave's rows) and 32 output columns (16 j + 4 (l / 16) + r), loaded at
+    // the start of each tile so that they have landed by its epilogue
+    constexpr bool ROW = SM == kSmRow;
+    constexpr int kRowRegs = ROW ? 8 : 1;
+    float rwa[kRowRegs];
+    float rwb[kRowRegs][4];
+    auto load_row_scales = [&](int tm_, int tn_) {
+        if constexpr (ROW) {
+            const float* pa = reinterpret_cast<const float*>(g.sa.s);
+            const float* pb = reinterpret_cast<const float*>(g.sb.s);
+            const bool ta = g.sa.gran == FP8Q_PER_TENSOR, tb = g.sb.gran == FP8Q_PER_TENSOR;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t m = (int64_t)tm_ * BM + wm + 16 * i + (l & 15);
+                rwa[i] = pa[ta ? 0 : (m < M ? m : M - 1)];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t n = (int64_t)tn_ * 256 + wn + 16 * j + 4 * (l >> 4) + r;
+                    rwb[j][r] = pb[tb ? 0 : (n < N ? n : N - 1)];
+                }
+        }
+    };
+    // acc[i][j] with its scales applied
+    auto scaled = [&](const v4f& a, int i, int j) -> v4f {
+        if constexpr (ROW) {
+            return v4f{a[0] * (rwa[i] * rwb[j][0]), a[1] * (rwa[i] * rwb[j][1]), a[2] * (rwa[i] * rwb[j][2]),
+                       a[3] * (rwa[i] * rwb[j][3])};
+        } else {
+            return a * S;
+        }
+    };
 
     v4f acc[8][8];
     v8i b[8];
@@ -552,6 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        load_row_scales(tm, tn);
         // this tile's first stage (and the previous tile's stores) complete
         vm_wait<0>();
         stage_barrier();
@@ -590,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
                 for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const v4f v = acc[2 * qq + ii][j] * S;
+                        const v4f v = scaled(acc[2 * qq + ii][j], 2 * qq + ii, j);
                         const v2bf_t p0 = __builtin_convertvector(v2f_t{v[0], v[1]}, v2bf_t);
                         const v2bf_t p1 = __builtin_convertvector(v2f_t{v[2], v[3]}, v2bf_t);
                         const int row = 16 * ii + (l & 15);
@@ -614,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<v4f*>(ep + (l & 15) * kEpPitch32 + (16 * j + 4 * (l >> 4)) * 4) = acc[i][j] * S;
+                    *reinterpret_cast<v4f*>(ep + (l & 15) * kEpPitch32 + (16 * j + 4 * (l >> 4)) * 4) = scaled(acc[i][j], i, j);
                 lds_wait_all();
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -659,11 +702,16 @@ static void launch_sm(const GemmArgs& g, int sm, hipStream_t s) {
     if (sm == kSmPerTensor && fast)
         hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmPerTensor>), dim3(persistent_grid()), dim3(kThreads), 0, s,
                            g, ntm, ntn);
+    else if (sm == kSmRow && fast)
+        hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmRow>), dim3(persistent_grid()), dim3(kThreads), 0, s, g,
+                           ntm, ntn);
     else if (sm == kSmMx && fast && g.K % 512 == 0)
         hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmMx>), dim3(persistent_grid()), dim3(kThreads), 0, s, g,
                            ntm, ntn);
     else if (sm == kSmPerTensor)
         hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmPerTensor, 256>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
+    else if (sm == kSmRow)
+        hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmRow, 256>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
     else
         hipLaunchKernelGGL((gemm_kernel<FA, FB, OUT, kSmMx, 256>), dim3(ntm * ntn), dim3(kThreads), 0, s, g, ntm, ntn);
 }
@@ -677,6 +725,7 @@ static void launch_out(const GemmArgs& g, int sm, hipStream_t s) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     int sm = kSmPerTensor;
     if (g.sa.gran == FP8Q_MX32) sm = kSmMx;
+    else if (g.sa.gran == FP8Q_ROWWISE || g.sb.gran == FP8Q_ROWWISE) sm = kSmRow;
     else if (g.sa.gran != FP8Q_PER_TENSOR || g.sb.gran != FP8Q_PER_TENSOR) sm = kSmBlock;
     if (g.fa == FP8Q_E4M3) {
         if (g.fb == FP8Q_E4M3) launch_out<FP8Q_E4M3, FP8Q_E4M3>(g, sm, s);

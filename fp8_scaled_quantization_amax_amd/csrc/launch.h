@@ -70,6 +70,13 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 // codes [rows, cols] -> [cols, rows]
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out, hipStream_t s);
 
+// Rowwise quantization: one fp32 scale per row (axis 0) or per column (axis
+// 1) into scales, codes into q [rows, cols], and (if qT != NULL) their
+// transpose into qT [cols, rows].  Axis 1 keeps integer maxima in `scales`
+// until its cast pass has converted them.
+hipError_t launch_quantize_rowwise(const void* x, int hp, int64_t rows, int64_t cols, int axis, int fmt, bool sat,
+                                   uint8_t* q, uint8_t* qT, float* scales, hipStream_t s);
+
 // Scaled GEMM on K-contiguous codes: C[M,N] = sum_k A[m,k] B[n,k] with scales.
 struct GemmScale {
     const void* s;     // float* or uint8_t* (E8M0)

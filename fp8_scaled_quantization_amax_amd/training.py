@@ -20,8 +20,8 @@ targets, loss and AdamW are plain torch ops around them.
 """
 import torch
 
-from . import (E4M3, E5M2, GemmOperand, fp8_gemm_scaled_NN, fp8_gemm_scaled_NT, fp8_gemm_scaled_TN,
-               fp8_quantize_per_tensor)
+from . import (E4M3, E5M2, ROWWISE, GemmOperand, fp8_gemm_scaled_NN, fp8_gemm_scaled_NT, fp8_gemm_scaled_TN,
+               fp8_quantize_per_tensor, fp8_quantize_rowwise)
 
 
 class FP8Matmul(torch.autograd.Function):
@@ -66,21 +66,80 @@ class FP8Matmul(torch.autograd.Function):
         return dx, dw
 
 
-def fp8_matmul(x, w):
-    """x . w^T through FP8Matmul."""
+class FP8MatmulRowwise(torch.autograd.Function):
+    """FP8Matmul with the lab page's "rowwise" recipe: every GEMM input scaled
+    per row along that GEMM's contraction, so each of x, w and dy is cast once
+    per GEMM it feeds:
+
+    - fprop NT: x and w per row;
+    - dgrad NN: dy per row, w per column (its K-major copy);
+    - wgrad TN: dy and x per column (K-major copies).
+
+    Each product is sum_k qa qb * sA[m] * sB[n]."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+            raise ValueError(f"FP8MatmulRowwise needs x[M,K] and w[N,K], got {tuple(x.shape)} and {tuple(w.shape)}")
+        if x.dtype != w.dtype or x.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"FP8MatmulRowwise needs x and w both fp32 or both bf16, got {x.dtype} and {w.dtype}")
+        x, w = x.contiguous(), w.contiguous()
+        M, K = x.shape
+        N = w.shape[0]
+        qx, _, sx = fp8_quantize_rowwise(x, 0, E4M3)
+        qw, _, sw = fp8_quantize_rowwise(w, 0, E4M3)
+        y = fp8_gemm_scaled_NT(M, N, K, GemmOperand.quantized(qx, E4M3, sx, ROWWISE),
+                               GemmOperand.quantized(qw, E4M3, sw, ROWWISE), x.dtype)
+        saved = []
+        if ctx.needs_input_grad[1]:    # wgrad: x per column (over tokens)
+            qx1, qx1T, sx1 = fp8_quantize_rowwise(x, 1, E4M3, emit_t=True)
+            saved += [qx1, qx1T, sx1]
+        if ctx.needs_input_grad[0]:    # dgrad: w per column (over output features)
+            qw1, qw1T, sw1 = fp8_quantize_rowwise(w, 1, E4M3, emit_t=True)
+            saved += [qw1, qw1T, sw1]
+        ctx.save_for_backward(*saved)
+        ctx.dtype, ctx.shape = x.dtype, (M, N, K)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        M, N, K = ctx.shape
+        saved = list(ctx.saved_tensors)
+        dy = dy.to(ctx.dtype).contiguous()
+        dx = dw = None
+        if ctx.needs_input_grad[1]:
+            qx1, qx1T, sx1 = saved[:3]
+            saved = saved[3:]
+            qg1, qg1T, sg1 = fp8_quantize_rowwise(dy, 1, E5M2, emit_t=True)
+            dw = fp8_gemm_scaled_TN(N, K, M, GemmOperand.quantized(qg1, E5M2, sg1, ROWWISE, kmajor=qg1T),
+                                    GemmOperand.quantized(qx1, E4M3, sx1, ROWWISE, kmajor=qx1T), ctx.dtype)
+        if ctx.needs_input_grad[0]:
+            qw1, qw1T, sw1 = saved[:3]
+            qg0, _, sg0 = fp8_quantize_rowwise(dy, 0, E5M2)
+            dx = fp8_gemm_scaled_NN(M, K, N, GemmOperand.quantized(qg0, E5M2, sg0, ROWWISE),
+                                    GemmOperand.quantized(qw1, E4M3, sw1, ROWWISE, kmajor=qw1T), ctx.dtype)
+        return dx, dw
+
+
+def fp8_matmul(x, w, recipe="tensorwise"):
+    """x . w^T through FP8Matmul ("tensorwise") or FP8MatmulRowwise ("rowwise")."""
+    if recipe == "rowwise":
+        return FP8MatmulRowwise.apply(x, w)
+    if recipe != "tensorwise":
+        raise ValueError(f"unknown recipe {recipe!r}")
     return FP8Matmul.apply(x, w)
 
 
-def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3):
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise"):
     """The lab page's check-[5] loop: the 2-layer MLP relu(X W1^T) W2^T is fitted
     to Y by mean squared error with AdamW(lr), with every matmul either FP8
-    (`fp8_matmul`) or plain fp32.  X, Y, W1 and W2 are device tensors; the
+    (`fp8_matmul` with `recipe`) or plain fp32.  X, Y, W1 and W2 are device tensors; the
     weights are copied and left unchanged.  Returns the list of per-step
     losses (floats, read once at the end)."""
     W1 = W1.detach().clone().requires_grad_()
     W2 = W2.detach().clone().requires_grad_()
     opt = torch.optim.AdamW([W1, W2], lr=lr)
-    mm = fp8_matmul if fp8 else (lambda a, b: a @ b.T)
+    mm = (lambda a, b: fp8_matmul(a, b, recipe)) if fp8 else (lambda a, b: a @ b.T)
     losses = []
     for _ in range(steps):
         loss = ((mm(torch.relu(mm(X, W1)), W2) - Y) ** 2).mean()

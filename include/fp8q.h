@@ -26,6 +26,9 @@
  *             entries); the current amax is recorded afterwards.  Smoke
  *             check [3]; SpikingJelly "Training and Inference Precision",
  *             recipe "delayed".
+ *   rowwise   one scale per row of each GEMM input along its contraction,
+ *             applied to the product as an outer product sA[m] * sB[n].  Lab
+ *             page, --recipe rowwise (torchao's rowwise Float8 recipe).
  *   granular  one scale per 1x128 tile (smoke check [4]), per 128x128 block
  *             (SpikingJelly recipe "block"; "How to Optimize
  *             Transformer-Based Models for Low-Precision Training", 2D block
@@ -49,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 1
+#define FP8Q_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 typedef enum fp8q_status {
@@ -73,7 +76,8 @@ typedef enum fp8q_gran {
     FP8Q_PER_TENSOR = 0,    /* one fp32 scale */
     FP8Q_TILE_1x128 = 1,    /* one fp32 scale per 128 consecutive elements along K */
     FP8Q_BLOCK_128x128 = 2, /* one fp32 scale per 128 x 128 block */
-    FP8Q_MX32 = 3           /* one E8M0 scale (2^(code-127)) per 32 elements along K */
+    FP8Q_MX32 = 3,          /* one E8M0 scale (2^(code-127)) per 32 elements along K */
+    FP8Q_ROWWISE = 4        /* one fp32 scale per operand row, over all of K */
 } fp8q_gran;
 
 /* Per-tensor scaling mode. */
@@ -187,6 +191,27 @@ int fp8_quantize_mx32(const void* x, int hp, int64_t rows, int64_t cols, int axi
                       int fmt, uint8_t* q, uint8_t* qT, uint8_t* e8m0,
                       unsigned flags, void* stream);
 
+/*
+ * Rowwise quantization with fp32 scales: the lab page's "rowwise" recipe,
+ * which scales each GEMM input per row along the contraction.
+ *   axis = 0: one scale per row, s_r = max(amax(row r) / fmax, 1e-12);
+ *             scales [rows].  q [rows, cols] is required; qT must be NULL.
+ *             This is the form of an operand whose contraction runs along
+ *             its stored columns (fprop x and w, dgrad's gradient).
+ *   axis = 1: one scale per column, s_c = max(amax(column c) / fmax, 1e-12);
+ *             scales [cols].  q [rows, cols] is required; qT [cols, rows] is
+ *             optional and holds the same codes K-major.  This is the form of
+ *             an operand whose contraction runs along its stored rows
+ *             (dgrad's weight, both wgrad operands).
+ * Every code: q = RNE_fp8(RN_fp32(x / s)) with its row's or column's s.
+ * Returns FP8Q_EINVAL for null x, q or scales, non-positive sizes, unknown
+ * enums or flags, and FP8Q_EUNSUPPORTED for a qT with axis 0.  With axis 1,
+ * `scales` holds integer maxima while the call runs.
+ */
+int fp8_quantize_rowwise(const void* x, int hp, int64_t rows, int64_t cols, int axis,
+                         int fmt, uint8_t* q, uint8_t* qT, float* scales,
+                         unsigned flags, void* stream);
+
 /* ---------------------------------------------------------------- GEMM */
 
 /*
@@ -203,6 +228,9 @@ int fp8_quantize_mx32(const void* x, int hp, int64_t rows, int64_t cols, int axi
  *   BLOCK_128x128  float [ceil(stored rows/128), ceil(stored cols/128)] in the
  *                  operand's STORED layout (one weight array serves fprop and dgrad)
  *   MX32           uint8 E8M0 [R, K/32], indexed like TILE_1x128
+ *   ROWWISE        float [R], one per operand row (what fp8_quantize_rowwise
+ *                  produces with axis 0 when K is the stored column axis,
+ *                  axis 1 when K is the stored row axis); pre-quantized only
  *   `data_kmajor` optionally holds the same codes already laid out [R, K]
  *   (K contiguous); if NULL and the stored layout is not K-contiguous, the
  *   library transposes the codes into the workspace.
@@ -249,7 +277,10 @@ size_t fp8_gemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
  * Alignment: M, N, K multiples of 16 (SpikingJelly alignment rule, lab page
  * module_filter_fn); K a multiple of 128 with TILE_1x128 / BLOCK_128x128
  * operands and of 32 with MX32.  Granularities: A and B each PER_TENSOR,
- * TILE_1x128 or BLOCK_128x128 in any combination, or both MX32.
+ * TILE_1x128 or BLOCK_128x128 in any combination, or both MX32, or ROWWISE
+ * with ROWWISE or PER_TENSOR (C = sum * sA[m] * sB[n], per-tensor scales
+ * broadcast).  ROWWISE operands must be pre-quantized (autocast with ROWWISE
+ * returns FP8Q_EUNSUPPORTED).
  * ws: fp8_gemm_workspace_bytes(...) bytes (may be NULL when that is 0),
  * zero-filled before its first use: autocast operands reduce in it, and its
  * completion counters must start at zero (every call leaves them at zero).

@@ -178,6 +178,15 @@ def quantize_tiles(x, axis, tile, fmt, saturate=False, mx=False):
     return q, sc
 
 
+def quantize_rowwise(x, axis, fmt, saturate=False):
+    """Rowwise scaling (the lab page's "rowwise" recipe): one scale per row
+    (axis 0) or per column (axis 1), i.e. a 1 x cols or rows x 1 tile.
+    Returns (codes [rows, cols], fp32 scales [rows] or [cols])."""
+    rows, cols = np.asarray(x).shape
+    q, sc = quantize_tiles(x, axis, cols if axis == 0 else rows, fmt, saturate)
+    return q, sc.reshape(-1)
+
+
 def quantize_blocks(x, br, bc, fmt, saturate=False):
     """br x bc block scaling; returns (codes, fp32 scales [ceil(rows/br), ceil(cols/bc)])."""
     x, hp = _hp(x)
@@ -207,6 +216,11 @@ class Scale:
             self.arr = np.array([value], dtype=np.float32)
         else:
             self.arr = np.ascontiguousarray(value, dtype=np.uint8 if e8m0 else np.float32)
+
+    @staticmethod
+    def rowwise(scales, K):
+        """One scale per operand row over all of K: the 1 x K tile of 'rowk'."""
+        return Scale("rowk", np.asarray(scales, np.float32).reshape(-1, 1), kblk=max(int(K), 1))
 
     def desc(self, rows, K):
         d = ScaleDesc()

@@ -16,7 +16,7 @@ loop on the CPU.
 import numpy as np
 import torch
 
-from . import E4M3, E5M2, Scale, gemm_nn, gemm_nt, gemm_tn, quantize_per_tensor
+from . import E4M3, E5M2, Scale, gemm_nn, gemm_nt, gemm_tn, quantize_per_tensor, quantize_rowwise
 
 
 def _q(t, fmt):
@@ -43,13 +43,48 @@ class OracleFP8Matmul(torch.autograd.Function):
         return dx, dw
 
 
-def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3):
+def _qr(t, fmt, axis, K):
+    q, s = quantize_rowwise(t.detach().contiguous().numpy(), axis, fmt)
+    return q, Scale.rowwise(s, K)
+
+
+class OracleFP8MatmulRowwise(torch.autograd.Function):
+    """The "rowwise" recipe: each GEMM input scaled per row along that GEMM's
+    contraction (x, w per row for fprop; dy per row and w per column for
+    dgrad; dy and x per column for wgrad)."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        M, K = x.shape
+        N = w.shape[0]
+        qx, sx = _qr(x, E4M3, 0, K)
+        qw, sw = _qr(w, E4M3, 0, K)
+        ctx.saved = (x.detach().clone(), w.detach().clone())
+        return torch.from_numpy(gemm_nt(qx, qw, E4M3, E4M3, sx, sw).astype(np.float32))
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w = ctx.saved
+        M, K = x.shape
+        N = w.shape[0]
+        qg0, sg0 = _qr(dy, E5M2, 0, N)
+        qw1, sw1 = _qr(w, E4M3, 1, N)
+        dx = torch.from_numpy(gemm_nn(qg0, qw1, E5M2, E4M3, sg0, sw1).astype(np.float32))
+        qg1, sg1 = _qr(dy, E5M2, 1, M)
+        qx1, sx1 = _qr(x, E4M3, 1, M)
+        dw = torch.from_numpy(gemm_tn(qg1, qx1, E5M2, E4M3, sg1, sx1).astype(np.float32))
+        return dx, dw
+
+
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise"):
     """Fit relu(X W1^T) W2^T to Y by mean squared error with AdamW(lr), every
-    matmul either OracleFP8Matmul or plain fp32; returns the per-step losses."""
+    matmul either the oracle's FP8 matmul of `recipe` or plain fp32; returns
+    the per-step losses."""
     W1 = W1.detach().clone().requires_grad_()
     W2 = W2.detach().clone().requires_grad_()
     opt = torch.optim.AdamW([W1, W2], lr=lr)
-    mm = OracleFP8Matmul.apply if fp8 else (lambda a, b: a @ b.T)
+    fp8_mm = OracleFP8MatmulRowwise.apply if recipe == "rowwise" else OracleFP8Matmul.apply
+    mm = fp8_mm if fp8 else (lambda a, b: a @ b.T)
     losses = []
     for _ in range(steps):
         loss = ((mm(torch.relu(mm(X, W1)), W2) - Y) ** 2).mean()

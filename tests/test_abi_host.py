@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fp8_amax", "fp8_quantize_per_tensor", "fp8_quantize_tile1x128", "fp8_quantize_block128x128",
-              "fp8_quantize_mx32", "fp8_gemm_scaled_NT", "fp8_gemm_scaled_NN", "fp8_gemm_scaled_TN",
+              "fp8_quantize_mx32", "fp8_quantize_rowwise", "fp8_gemm_scaled_NT", "fp8_gemm_scaled_NN", "fp8_gemm_scaled_TN",
               "fp8_gemm_workspace_bytes", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version",
               "fp8q_reduce_workspace_bytes"):
         assert n in names
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_abi_version() == 1
+    assert L.fp8q_abi_version() == 2
     assert L.fp8q_status_string(0) == b"ok"
     for s in range(1, 7):
         assert L.fp8q_status_string(s) not in (b"ok", b"unknown status")
@@ -73,6 +73,10 @@ def test_invalid_arguments_are_rejected_before_any_gpu_call():
     assert L.fp8_quantize_tile1x128(fake, fq.BF16, 4, 4, 2, 0, fake, None, fake, 0, None) == fq.EINVAL
     assert L.fp8_quantize_mx32(fake, fq.BF16, 4, 4, 0, 0, fake, None, None, 0, None) == fq.EINVAL
     assert L.fp8_quantize_block128x128(fake, fq.F32, -1, 4, 0, fake, None, fake, 0, None) == fq.EINVAL
+    # rowwise: bad axis, missing scales, a transposed copy with axis 0
+    assert L.fp8_quantize_rowwise(fake, fq.BF16, 4, 4, 2, 0, fake, None, fake, 0, None) == fq.EINVAL
+    assert L.fp8_quantize_rowwise(fake, fq.BF16, 4, 4, 0, 0, fake, None, None, 0, None) == fq.EINVAL
+    assert L.fp8_quantize_rowwise(fake, fq.BF16, 4, 4, 0, 0, fake, fake, fake, 0, None) == fq.EUNSUPPORTED
 
 
 def _op(**kw):
@@ -96,6 +100,12 @@ def test_gemm_validation():
     assert L.fp8_gemm_scaled_NT(64, 64, 48, R(Am), R(Bm), fake, fq.BF16, None, 0, None) == fq.EALIGN
     # MX on one side only is not implemented (and never silently substituted)
     assert L.fp8_gemm_scaled_NT(64, 64, 64, R(Am), R(B), fake, fq.BF16, None, 0, None) == fq.EUNSUPPORTED
+    # rowwise combines with rowwise or per-tensor only, and needs pre-quantized codes
+    Ar = _op(granularity=fq.ROWWISE)
+    assert L.fp8_gemm_scaled_NT(64, 64, 128, R(Ar), R(At), fake, fq.BF16, None, 0, None) == fq.EUNSUPPORTED
+    Ara = _op(quantized=0, hp=fq.BF16, granularity=fq.ROWWISE)
+    assert L.fp8_gemm_scaled_NT(64, 64, 64, R(Ara), R(B), fake, fq.BF16, None, 0, None) == fq.EUNSUPPORTED
+    assert L.fp8_gemm_workspace_bytes(0, 256, 256, 256, R(Ar), R(B)) == 0
     # delayed scaling is per-tensor only
     Ad = _op(quantized=0, hp=fq.BF16, scaling=fq.DELAYED, granularity=fq.TILE_1x128, state=0x50000)
     assert L.fp8_gemm_scaled_NT(64, 64, 128, R(Ad), R(B), fake, fq.BF16, None, 0, None) == fq.EUNSUPPORTED

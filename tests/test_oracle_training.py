@@ -61,3 +61,39 @@ def test_first_step_loss_is_quantized_but_close(losses):
     l32, l8 = losses
     assert l8[0] != l32[0]
     assert abs(l8[0] - l32[0]) / l32[0] < 0.05
+
+
+def _fake_quant_rows(x, dtype, fmax, dim):
+    # per-row (dim=1: max over each row) or per-column (dim=0) scaled round trip
+    # with torch's float8 casts
+    s = (x.abs().amax(dim=dim, keepdim=True) / fmax).clamp_min(1e-12)
+    return (x / s).to(dtype).float() * s
+
+
+def test_rowwise_one_step_matches_fake_quant_formulas():
+    """The rowwise recipe: y = xq . wq^T with x and w scaled per row; dx = gq . wq'
+    with dy per row and w per column; dw = gq'^T . xq' with dy and x per column."""
+    d = workloads.lab_mlp_inputs()
+    x = torch.relu(d["X"] @ d["W1"].T).requires_grad_()
+    w = d["W2"].clone().requires_grad_()
+    y = fp8_train.OracleFP8MatmulRowwise.apply(x, w)
+    g = torch.randn(y.shape, generator=torch.Generator().manual_seed(5)) * 1e-3
+    y.backward(g)
+    e4, e5 = torch.float8_e4m3fn, torch.float8_e5m2
+    xd, wd = x.detach(), w.detach()
+    y_ref = _fake_quant_rows(xd, e4, E4M3_MAX, 1).double() @ _fake_quant_rows(wd, e4, E4M3_MAX, 1).double().T
+    dx_ref = _fake_quant_rows(g, e5, E5M2_MAX, 1).double() @ _fake_quant_rows(wd, e4, E4M3_MAX, 0).double()
+    dw_ref = _fake_quant_rows(g, e5, E5M2_MAX, 0).double().T @ _fake_quant_rows(xd, e4, E4M3_MAX, 0).double()
+    for got, ref in ((y.detach(), y_ref), (x.grad, dx_ref), (w.grad, dw_ref)):
+        assert got.shape == ref.shape
+        err = (got.double() - ref).abs().max().item()
+        assert err <= 1e-6 * ref.abs().max().item(), (err, ref.abs().max().item())
+
+
+def test_rowwise_lab_check5_final_loss_gap():
+    """Check [5]'s bound applied to the rowwise recipe."""
+    d = workloads.lab_mlp_inputs()
+    l32 = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=False)
+    lr = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=True, recipe="rowwise")
+    assert abs(lr[-1] - l32[-1]) / l32[-1] < 0.10
+    assert lr[-1] < 0.5 * lr[0]

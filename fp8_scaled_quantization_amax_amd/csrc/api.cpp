@@ -399,6 +399,30 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, i
     return ok();
 }
 
+int fp8_quantize_per_tensor_sr(const void* x, int hp, int64_t rows, int64_t cols, int fmt, uint64_t seed,
+                               uint64_t offset, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
+                               unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+    int r;
+    if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags)) != FP8Q_OK) return r;
+    if (scale_out == nullptr) return fail(FP8Q_EINVAL, "scale_out is required");
+    if (ws == nullptr || ws_bytes < fp8q::kReduceWsBytes)
+        return fail(FP8Q_EWORKSPACE, "reduce workspace of %zu bytes needed", fp8q::kReduceWsBytes);
+    if ((r = check_device()) != FP8Q_OK) return r;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    float* partials = reinterpret_cast<float*>(ws);
+    const int nparts = fp8q::amax_partials_grid(rows * cols);
+    if ((r = launched(fp8q::launch_amax_partials(x, hp, rows * cols, partials, nparts, nullptr, s), "amax")) !=
+        FP8Q_OK)
+        return r;
+    if ((r = launched(fp8q::launch_quantize_sr(x, hp, rows * cols, fmt, (flags & FP8Q_SATURATE) != 0, seed, offset,
+                                               partials, nparts, q, scale_out, amax_out, s),
+                      "quantize")) != FP8Q_OK)
+        return r;
+    if (qT != nullptr && (r = launched(fp8q::launch_transpose_u8(q, rows, cols, qT, s), "transpose")) != FP8Q_OK)
+        return r;
+    return ok();
+}
+
 int fp8_quantize_tile1x128(const void* x, int hp, int64_t rows, int64_t cols, int axis, int fmt, uint8_t* q,
                            uint8_t* qT, float* scales, unsigned flags, void* stream) {
     int r;

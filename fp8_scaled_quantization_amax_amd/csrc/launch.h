@@ -70,6 +70,13 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 // codes [rows, cols] -> [cols, rows]
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out, hipStream_t s);
 
+// Per-tensor current scaling with a stochastically rounded cast: the scale
+// from the amax partials (as the current-scaling cast), element i rounded with
+// word i mod 4 of Philox4x32-10(counter (i / 4, offset), key seed).
+hipError_t launch_quantize_sr(const void* x, int hp, int64_t n, int fmt, bool sat, uint64_t seed, uint64_t offset,
+                              const float* partials, int nparts, uint8_t* q, float* scale_out, float* amax_out,
+                              hipStream_t s);
+
 // Rowwise quantization: one fp32 scale per row (axis 0) or per column (axis
 // 1) into scales, codes into q [rows, cols], and (if qT != NULL) their
 // transpose into qT [cols, rows].  Axis 1 keeps integer maxima in `scales`

@@ -1,0 +1,178 @@
+// Stochastically rounded FP8 cast with per-tensor current scaling, for gfx950.
+//
+// The low-precision training recipe of "How to Optimize Transformer-Based
+// Models for Low-Precision Training" rounds its gradients stochastically;
+// this applies that to the 8-bit formats.  The scale is the one of the
+// "fp8_parity.py" lab page's scaled_roundtrip (amax / fmax, floored at 1e-12),
+// and the quotient v = RN32(x / s) is then rounded to one of its two
+// neighbouring grid values: with D the grid spacing at |v| and f the position
+// of |v| between n D and (n + 1) D, it goes up when r + floor(f 2^32) >= 2^32
+// for the element's random word r.  The words come from the counter-based
+// generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC 2011), so a (seed, offset) pair fixes
+// every decision: element i takes word i mod 4 of the block for counter
+// (i / 4, offset) and key seed.
+//
+// Design: the amax pass is the shared partial-maximum grid; this kernel
+// folds the partials into the scale (every block), then each thread takes
+// groups of 4 elements, one generator call per group.  The generator's ten
+// rounds of 32 x 32 -> 64-bit multiplies cost more VALU time than the HBM
+// traffic of the group, so the kernel is ALU-bound.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8q {
+
+// Philox4x32-10: ten rounds of (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0) with
+// (hi0, lo0) = 0xD2511F53 * c0 and (hi1, lo1) = 0xCD9E8D57 * c2; the key gains
+// 0x9E3779B9 and 0xBB67AE85 before each round after the first.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+// Stochastic rounding of a finite v to the format's grid with the word r (the
+// result is exactly a grid value, or the step past the largest one, which the
+// converter then overflows like any other value); NaN and Inf pass unchanged.
+// |v| = M 2^(e - 23) with the 24-bit significand M; the grid spacing is
+// 2^D with D = max(e, emin) - mantissa bits, so |v| / 2^D = M / 2^shift.
+template <int FMT>
+__device__ __forceinline__ float sr_round(float v, uint32_t r) {
+    constexpr int MB = FMT == FP8Q_E4M3 ? 3 : 2;
+    constexpr int EMIN = FMT == FP8Q_E4M3 ? -6 : -14;
+    const uint32_t ab = __float_as_uint(v) & 0x7fffffffu;
+    if (ab >= 0x7f800000u) return v;
+    const bool normal = ab >= 0x00800000u;
+    const uint32_t M = (ab & 0x7fffffu) | (normal ? 0x800000u : 0u);
+    const int e = normal ? (int)(ab >> 23) - 127 : -126;
+    const int D = (e > EMIN ? e : EMIN) - MB;
+    const int shift = D - (e - 23);   // at least 23 - MB
+    uint32_t n = 0, frac32 = 0;       // |v| / 2^D = n + frac32 / 2^32 (+ less than 2^-32)
+    if (shift < 24) {
+        n = M >> shift;
+        frac32 = (M & ((1u << shift) - 1u)) << (32 - shift);
+    } else if (shift <= 32) {
+        frac32 = M << (32 - shift);
+    } else if (shift < 56) {
+        frac32 = M >> (shift - 32);
+    }
+    const uint32_t up = r > 0xffffffffu - frac32 ? 1u : 0u;   // r + frac32 >= 2^32
+    const float mag = (float)(n + up) * __uint_as_float((uint32_t)(D + 127) << 23);
+    return __builtin_copysignf(mag, v);
+}
+
+template <int HP>
+__device__ __forceinline__ float load_one_sr(const void* __restrict__ x, int64_t i) {
+    if constexpr (HP == FP8Q_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[i]);
+    else return reinterpret_cast<const float*>(x)[i];
+}
+
+// VEC: n % 4 == 0 is not needed (the tail group is scalar), but x must be
+// aligned to 4 elements and q to 4 bytes.
+template <int HP, int FMT, bool SAT, bool VEC>
+__global__ __launch_bounds__(256) void quantize_sr_kernel(const void* __restrict__ x, int64_t n,
+                                                          const float* __restrict__ partials, int nparts,
+                                                          uint32_t k0, uint32_t k1, uint32_t o0, uint32_t o1,
+                                                          uint8_t* __restrict__ q, float* scale_out,
+                                                          float* amax_out) {
+    __shared__ uint32_t red[4];
+    const float amax = reduce_partials_256(partials, nparts, red);
+    const float s = scale_from_amax<FMT>(amax);
+    const float rc = 1.0f / s;
+    const int64_t ngroups = (n + 3) / 4;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < ngroups; g += (int64_t)gridDim.x * 256) {
+        const uint4 rw = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), o0, o1, k0, k1);
+        const uint32_t rr[4] = {rw.x, rw.y, rw.z, rw.w};
+        const int64_t i0 = 4 * g;
+        const bool full = i0 + 4 <= n;
+        float v[4];
+        if (VEC && full) {
+            if constexpr (HP == FP8Q_BF16) {
+                const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + i0);
+                v[0] = __uint_as_float(w.x << 16);
+                v[1] = __uint_as_float(w.x & 0xffff0000u);
+                v[2] = __uint_as_float(w.y << 16);
+                v[3] = __uint_as_float(w.y & 0xffff0000u);
+            } else {
+                const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i0);
+                v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = i0 + e < n ? load_one_sr<HP>(x, i0 + e) : 0.0f;
+        }
+        float c[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] = saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[e], s, rc), rr[e]));
+        const uint32_t w = pack4<FMT>(c[0], c[1], c[2], c[3]);
+        if (VEC && full) {
+            *reinterpret_cast<uint32_t*>(q + i0) = w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (i0 + e < n) q[i0 + e] = (uint8_t)((w >> (8 * e)) & 0xffu);
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *scale_out = s;
+        if (amax_out) *amax_out = amax;
+    }
+}
+
+template <int HP, int FMT, bool SAT>
+static void launch_sr_t(const void* x, int64_t n, const float* partials, int nparts, uint64_t seed, uint64_t offset,
+                        uint8_t* q, float* scale_out, float* amax_out, bool vec, hipStream_t s) {
+    const int64_t ngroups = (n + 3) / 4;
+    const int64_t want = (ngroups + 255) / 256;
+    const int grid = (int)(want < 4096 ? (want < 1 ? 1 : want) : 4096);
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32), o0 = (uint32_t)offset,
+                   o1 = (uint32_t)(offset >> 32);
+    if (vec)
+        hipLaunchKernelGGL((quantize_sr_kernel<HP, FMT, SAT, true>), dim3(grid), dim3(256), 0, s, x, n, partials,
+                           nparts, k0, k1, o0, o1, q, scale_out, amax_out);
+    else
+        hipLaunchKernelGGL((quantize_sr_kernel<HP, FMT, SAT, false>), dim3(grid), dim3(256), 0, s, x, n, partials,
+                           nparts, k0, k1, o0, o1, q, scale_out, amax_out);
+}
+
+hipError_t launch_quantize_sr(const void* x, int hp, int64_t n, int fmt, bool sat, uint64_t seed, uint64_t offset,
+                              const float* partials, int nparts, uint8_t* q, float* scale_out, float* amax_out,
+                              hipStream_t s) {
+    const bool vec = (uintptr_t)x % (hp == FP8Q_BF16 ? 8 : 16) == 0 && (uintptr_t)q % 4 == 0;
+    if (hp == FP8Q_BF16) {
+        if (fmt == FP8Q_E4M3) {
+            if (sat) launch_sr_t<FP8Q_BF16, FP8Q_E4M3, true>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+            else launch_sr_t<FP8Q_BF16, FP8Q_E4M3, false>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+        } else {
+            if (sat) launch_sr_t<FP8Q_BF16, FP8Q_E5M2, true>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+            else launch_sr_t<FP8Q_BF16, FP8Q_E5M2, false>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+        }
+    } else {
+        if (fmt == FP8Q_E4M3) {
+            if (sat) launch_sr_t<FP8Q_F32, FP8Q_E4M3, true>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+            else launch_sr_t<FP8Q_F32, FP8Q_E4M3, false>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+        } else {
+            if (sat) launch_sr_t<FP8Q_F32, FP8Q_E5M2, true>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+            else launch_sr_t<FP8Q_F32, FP8Q_E5M2, false>(x, n, partials, nparts, seed, offset, q, scale_out, amax_out, vec, s);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fp8q

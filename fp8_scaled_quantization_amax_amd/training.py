@@ -21,17 +21,19 @@ targets, loss and AdamW are plain torch ops around them.
 import torch
 
 from . import (E4M3, E5M2, ROWWISE, GemmOperand, fp8_gemm_scaled_NN, fp8_gemm_scaled_NT, fp8_gemm_scaled_TN,
-               fp8_quantize_per_tensor, fp8_quantize_rowwise)
+               fp8_quantize_per_tensor, fp8_quantize_per_tensor_sr, fp8_quantize_rowwise)
 
 
 class FP8Matmul(torch.autograd.Function):
     """y[M,N] = x[M,K] . w[N,K]^T in FP8 (E4M3 forward, E5M2 output gradient).
 
     x and w are fp32 or bf16 (the same dtype); y, dx and dw come out in that
-    dtype (fp32 accumulation, one rounding at the end)."""
+    dtype (fp32 accumulation, one rounding at the end).  With sr = (seed,
+    offset) the output gradient is rounded stochastically
+    (fp8_quantize_per_tensor_sr) instead of to nearest."""
 
     @staticmethod
-    def forward(ctx, x, w):
+    def forward(ctx, x, w, sr=None):
         if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
             raise ValueError(f"FP8Matmul needs x[M,K] and w[N,K], got {tuple(x.shape)} and {tuple(w.shape)}")
         if x.dtype != w.dtype or x.dtype not in (torch.float32, torch.bfloat16):
@@ -46,7 +48,7 @@ class FP8Matmul(torch.autograd.Function):
         y = fp8_gemm_scaled_NT(M, N, K, GemmOperand.quantized(qx, E4M3, sx),
                                GemmOperand.quantized(qw, E4M3, sw), x.dtype)
         ctx.save_for_backward(qx, qxT, sx, qw, qwT, sw)
-        ctx.dtype = x.dtype
+        ctx.dtype, ctx.sr = x.dtype, sr
         return y
 
     @staticmethod
@@ -55,7 +57,10 @@ class FP8Matmul(torch.autograd.Function):
         dy = dy.to(ctx.dtype).contiguous()
         M, N = dy.shape
         K = qx.shape[1]
-        qg, qgT, sg, _ = fp8_quantize_per_tensor(dy, E5M2, emit_t=True)
+        if ctx.sr is None:
+            qg, qgT, sg, _ = fp8_quantize_per_tensor(dy, E5M2, emit_t=True)
+        else:
+            qg, qgT, sg, _ = fp8_quantize_per_tensor_sr(dy, E5M2, ctx.sr[0], ctx.sr[1], emit_t=True)
         dx = dw = None
         if ctx.needs_input_grad[0]:
             dx = fp8_gemm_scaled_NN(M, K, N, GemmOperand.quantized(qg, E5M2, sg),
@@ -63,7 +68,7 @@ class FP8Matmul(torch.autograd.Function):
         if ctx.needs_input_grad[1]:
             dw = fp8_gemm_scaled_TN(N, K, M, GemmOperand.quantized(qg, E5M2, sg, kmajor=qgT),
                                     GemmOperand.quantized(qx, E4M3, sx, kmajor=qxT), ctx.dtype)
-        return dx, dw
+        return dx, dw, None
 
 
 class FP8MatmulRowwise(torch.autograd.Function):
@@ -121,28 +126,35 @@ class FP8MatmulRowwise(torch.autograd.Function):
         return dx, dw
 
 
-def fp8_matmul(x, w, recipe="tensorwise"):
-    """x . w^T through FP8Matmul ("tensorwise") or FP8MatmulRowwise ("rowwise")."""
+def fp8_matmul(x, w, recipe="tensorwise", sr=None):
+    """x . w^T through FP8Matmul ("tensorwise", optionally with stochastically
+    rounded gradients: sr = (seed, offset)) or FP8MatmulRowwise ("rowwise")."""
     if recipe == "rowwise":
+        if sr is not None:
+            raise ValueError("stochastic rounding is implemented for the tensorwise recipe")
         return FP8MatmulRowwise.apply(x, w)
     if recipe != "tensorwise":
         raise ValueError(f"unknown recipe {recipe!r}")
-    return FP8Matmul.apply(x, w)
+    return FP8Matmul.apply(x, w, sr)
 
 
-def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise"):
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None):
     """The lab page's check-[5] loop: the 2-layer MLP relu(X W1^T) W2^T is fitted
     to Y by mean squared error with AdamW(lr), with every matmul either FP8
-    (`fp8_matmul` with `recipe`) or plain fp32.  X, Y, W1 and W2 are device tensors; the
+    (`fp8_matmul` with `recipe`; with grad_sr_seed, output gradients rounded
+    stochastically, offset 2 step + layer) or plain fp32.  X, Y, W1 and W2 are device tensors; the
     weights are copied and left unchanged.  Returns the list of per-step
     losses (floats, read once at the end)."""
     W1 = W1.detach().clone().requires_grad_()
     W2 = W2.detach().clone().requires_grad_()
     opt = torch.optim.AdamW([W1, W2], lr=lr)
-    mm = (lambda a, b: fp8_matmul(a, b, recipe)) if fp8 else (lambda a, b: a @ b.T)
+    def mm(a, b, t, j):
+        if not fp8:
+            return a @ b.T
+        return fp8_matmul(a, b, recipe, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j))
     losses = []
-    for _ in range(steps):
-        loss = ((mm(torch.relu(mm(X, W1)), W2) - Y) ** 2).mean()
+    for t in range(steps):
+        loss = ((mm(torch.relu(mm(X, W1, t, 0)), W2, t, 1) - Y) ** 2).mean()
         opt.zero_grad()
         loss.backward()
         opt.step()

@@ -158,6 +158,29 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols,
                             unsigned flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Per-tensor current scaling with a stochastically rounded cast (the
+ * gradient rounding of "How to Optimize Transformer-Based Models for
+ * Low-Precision Training", applied to the 8-bit formats).
+ * s = max(amax / fmax, 1e-12) as fp8_quantize_per_tensor; v = RN32(x / s);
+ * v lies between the grid values n D and (n + 1) D (D the grid spacing at
+ * |v|, f = |v| / D - n) and becomes (n + 1) D, with the sign of v, when
+ * r + floor(f * 2^32) >= 2^32, else n D; the result is encoded as a cast is
+ * (overflow rule and FP8Q_SATURATE as above; NaN stays NaN).
+ * r for element i (row-major) is word i mod 4 of Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC
+ * 2011) with counter (low, high 32 bits of i / 4, low, high 32 bits of
+ * offset) and key (low, high 32 bits of seed): equal (seed, offset) give
+ * equal codes; callers advance offset (or seed) between steps.
+ * q [rows, cols] is required; qT [cols, rows] optional; ws, ws_bytes: the
+ * reduce workspace as for fp8_quantize_per_tensor.  Errors as
+ * fp8_quantize_per_tensor.
+ */
+int fp8_quantize_per_tensor_sr(const void* x, int hp, int64_t rows, int64_t cols, int fmt,
+                               uint64_t seed, uint64_t offset,
+                               uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
+                               unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * 1x128 tile quantization with fp32 scales (lab page smoke check [4]).
  *   axis = 0: tiles of 128 consecutive columns of a row;
  *             scales [rows, ceil(cols/128)].

@@ -54,6 +54,12 @@ def lib():
         L.orc_gemm.argtypes = [I64, I64, I64, P, I64, I64, I32, ctypes.POINTER(ScaleDesc),
                                P, I64, I64, I32, ctypes.POINTER(ScaleDesc), P, I64, P]
         L.orc_encode_array.restype, L.orc_encode_array.argtypes = None, [P, I64, I32, I32, P]
+        U32, U64 = ctypes.c_uint32, ctypes.c_uint64
+        L.orc_philox4x32_10.restype, L.orc_philox4x32_10.argtypes = None, [P, P, P]
+        L.orc_sr_word.restype, L.orc_sr_word.argtypes = U32, [U64, U64, U64]
+        L.orc_encode_sr.restype, L.orc_encode_sr.argtypes = ctypes.c_uint8, [F, U32, I32, I32]
+        L.orc_quantize_per_tensor_sr.restype = None
+        L.orc_quantize_per_tensor_sr.argtypes = [P, I32, I64, I32, I32, U64, U64, P, P, P]
         L.orc_encode_compare_range.restype = I64
         L.orc_encode_compare_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, P,
                                                ctypes.POINTER(ctypes.c_uint64)]
@@ -134,6 +140,34 @@ def quantize_per_tensor(x, fmt, saturate=False):
     s = np.zeros(1, np.float32)
     a = np.zeros(1, np.float32)
     lib().orc_quantize_per_tensor(_ptr(x), hp, x.size, fmt, int(saturate), _ptr(q), _ptr(s), _ptr(a))
+    return q, s[0], a[0]
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of a 4-word counter and a 2-word key -> 4 words."""
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_word(seed, offset, i):
+    return int(lib().orc_sr_word(int(seed), int(offset), int(i)))
+
+
+def encode_sr(v, r, fmt, saturate=False):
+    return int(lib().orc_encode_sr(float(v), int(r) & 0xFFFFFFFF, fmt, int(saturate)))
+
+
+def quantize_per_tensor_sr(x, fmt, seed, offset=0, saturate=False):
+    """Current scaling with a stochastically rounded cast: (codes, scale, amax)."""
+    x, hp = _hp(x)
+    q = np.empty(x.shape, dtype=np.uint8)
+    s = np.zeros(1, np.float32)
+    a = np.zeros(1, np.float32)
+    lib().orc_quantize_per_tensor_sr(_ptr(x), hp, x.size, fmt, int(saturate), int(seed), int(offset), _ptr(q),
+                                     _ptr(s), _ptr(a))
     return q, s[0], a[0]
 
 

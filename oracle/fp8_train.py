@@ -16,7 +16,7 @@ loop on the CPU.
 import numpy as np
 import torch
 
-from . import E4M3, E5M2, Scale, gemm_nn, gemm_nt, gemm_tn, quantize_per_tensor, quantize_rowwise
+from . import E4M3, E5M2, Scale, gemm_nn, gemm_nt, gemm_tn, quantize_per_tensor, quantize_per_tensor_sr, quantize_rowwise
 
 
 def _q(t, fmt):
@@ -25,22 +25,28 @@ def _q(t, fmt):
 
 
 class OracleFP8Matmul(torch.autograd.Function):
-    """y = x . w^T with E4M3 inputs forward and an E5M2 output gradient backward."""
+    """y = x . w^T with E4M3 inputs forward and an E5M2 output gradient backward
+    (rounded stochastically with sr = (seed, offset))."""
 
     @staticmethod
-    def forward(ctx, x, w):
+    def forward(ctx, x, w, sr=None):
         qx, sx = _q(x, E4M3)
         qw, sw = _q(w, E4M3)
         ctx.saved = (qx, sx, qw, sw)
+        ctx.sr = sr
         return torch.from_numpy(gemm_nt(qx, qw, E4M3, E4M3, sx, sw).astype(np.float32))
 
     @staticmethod
     def backward(ctx, dy):
         qx, sx, qw, sw = ctx.saved
-        qg, sg = _q(dy, E5M2)
+        if ctx.sr is None:
+            qg, sg = _q(dy, E5M2)
+        else:
+            qg, s, _ = quantize_per_tensor_sr(dy.detach().contiguous().numpy(), E5M2, ctx.sr[0], ctx.sr[1])
+            sg = Scale("tensor", s)
         dx = torch.from_numpy(gemm_nn(qg, qw, E5M2, E4M3, sg, sw).astype(np.float32))
         dw = torch.from_numpy(gemm_tn(qg, qx, E5M2, E4M3, sg, sx).astype(np.float32))
-        return dx, dw
+        return dx, dw, None
 
 
 def _qr(t, fmt, axis, K):
@@ -76,18 +82,22 @@ class OracleFP8MatmulRowwise(torch.autograd.Function):
         return dx, dw
 
 
-def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise"):
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None):
     """Fit relu(X W1^T) W2^T to Y by mean squared error with AdamW(lr), every
     matmul either the oracle's FP8 matmul of `recipe` or plain fp32; returns
     the per-step losses."""
     W1 = W1.detach().clone().requires_grad_()
     W2 = W2.detach().clone().requires_grad_()
     opt = torch.optim.AdamW([W1, W2], lr=lr)
-    fp8_mm = OracleFP8MatmulRowwise.apply if recipe == "rowwise" else OracleFP8Matmul.apply
-    mm = fp8_mm if fp8 else (lambda a, b: a @ b.T)
+    def mm(a, b, t, j):
+        if not fp8:
+            return a @ b.T
+        if recipe == "rowwise":
+            return OracleFP8MatmulRowwise.apply(a, b)
+        return OracleFP8Matmul.apply(a, b, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j))
     losses = []
-    for _ in range(steps):
-        loss = ((mm(torch.relu(mm(X, W1)), W2) - Y) ** 2).mean()
+    for t in range(steps):
+        loss = ((mm(torch.relu(mm(X, W1, t, 0)), W2, t, 1) - Y) ** 2).mean()
         opt.zero_grad()
         loss.backward()
         opt.step()

@@ -223,6 +223,95 @@ void orc_quantize_delayed(const void* x, int hp, int64_t n, int fmt, int saturat
 }
 
 /* ------------------------------------------------------------------ */
+/* Stochastic rounding of a cast ([BLOG]: the low-precision recipe rounds */
+/* its gradients stochastically; applied here to the 8-bit formats).      */
+/* ------------------------------------------------------------------ */
+
+/* Philox4x32-10 counter-based generator (Salmon, Moraes, Dror, Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): ten rounds; a
+ * round multiplies counter words 0 and 2 by 0xD2511F53 and 0xCD9E8D57 (32 x
+ * 32 -> 64 bits) and forms (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key
+ * grows by the Weyl increments 0x9E3779B9, 0xBB67AE85 before every round
+ * after the first. */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    int r;
+    for (r = 0; r < 10; ++r) {
+        uint64_t p0, p1;
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        p0 = (uint64_t)0xD2511F53u * c0;
+        p1 = (uint64_t)0xCD9E8D57u * c2;
+        c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        c1 = (uint32_t)p1;
+        c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c3 = (uint32_t)p0;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Random word of element i (reading, in the design notes): word i mod 4 of
+ * Philox4x32-10 with counter (low, high half of i / 4, low, high half of
+ * offset) and key (low, high half of seed). */
+uint32_t orc_sr_word(uint64_t seed, uint64_t offset, uint64_t i)
+{
+    const uint64_t g = i >> 2;
+    const uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    orc_philox4x32_10(ctr, key, out);
+    return out[i & 3];
+}
+
+/* Stochastic rounding of v with the random word r (reading, in the design
+ * notes).  |v| lies in [n D, (n + 1) D) for the grid spacing D at |v|
+ * (2^(max(floor(log2|v|), 1 - bias) - mantissa bits)); with
+ * f = |v| / D - n, the magnitude becomes (n + 1) D when
+ * r + floor(f * 2^32) >= 2^32 -- probability floor(f * 2^32) / 2^32 for a
+ * uniform r -- and n D otherwise.  The sign is kept and the result encoded
+ * as a cast is (so a step past the largest finite value overflows like a
+ * cast).  NaN and +-Inf are encoded unchanged. */
+uint8_t orc_encode_sr(float v, uint32_t r, int fmt, int saturate)
+{
+    double a, D, n, f;
+    uint64_t frac32;
+    int e;
+    if (isnan(v) || isinf(v)) return orc_encode(v, fmt, saturate);
+    a = fabs((double)v);
+    e = 1 - fmt_bias(fmt);
+    if (a != 0.0) {
+        int ea;
+        frexp(a, &ea);          /* a = m 2^ea, m in [0.5, 1): floor(log2 a) = ea - 1 */
+        if (ea - 1 > e) e = ea - 1;
+    }
+    D = ldexp(1.0, e - fmt_mbits(fmt));
+    n = floor(a / D);           /* a / D exact: D is a power of two */
+    f = a / D - n;
+    frac32 = (uint64_t)floor(ldexp(f, 32));
+    if ((uint64_t)r + frac32 >= ((uint64_t)1 << 32)) n += 1.0;
+    return orc_encode((float)copysign(n * D, (double)v), fmt, saturate);
+}
+
+/* Per-tensor current scaling with a stochastically rounded cast: amax and
+ * scale as orc_quantize_per_tensor, then q_i = encode_sr(RN32(x_i / s),
+ * word(seed, offset, i)). */
+void orc_quantize_per_tensor_sr(const void* x, int hp, int64_t n, int fmt, int saturate, uint64_t seed,
+                                uint64_t offset, uint8_t* q, float* scale_out, float* amax_out)
+{
+    const float amax = orc_amax(x, hp, n);
+    const float s = orc_scale_from_amax(amax, fmt);
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i)
+        q[i] = orc_encode_sr(div_rn32(load_hp(x, hp, i), s), orc_sr_word(seed, offset, (uint64_t)i), fmt, saturate);
+    if (scale_out) *scale_out = s;
+    if (amax_out) *amax_out = amax;
+}
+
+/* ------------------------------------------------------------------ */
 /* Granular scaling: 1 x T tiles ([LAB] check [4]: scaled_roundtrip per   */
 /* 128-wide row), T x 1 tiles, Br x Bc blocks ([SJ] "block"; [BLOG] 2D    */
 /* block scaling for weights), MX blocks of 32 with an E8M0 power-of-two  */

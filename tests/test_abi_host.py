@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fp8_amax", "fp8_quantize_per_tensor", "fp8_quantize_tile1x128", "fp8_quantize_block128x128",
-              "fp8_quantize_mx32", "fp8_quantize_rowwise", "fp8_gemm_scaled_NT", "fp8_gemm_scaled_NN", "fp8_gemm_scaled_TN",
+              "fp8_quantize_mx32", "fp8_quantize_rowwise", "fp8_quantize_per_tensor_sr", "fp8_gemm_scaled_NT", "fp8_gemm_scaled_NN", "fp8_gemm_scaled_TN",
               "fp8_gemm_workspace_bytes", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version",
               "fp8q_reduce_workspace_bytes"):
         assert n in names
@@ -73,6 +73,11 @@ def test_invalid_arguments_are_rejected_before_any_gpu_call():
     assert L.fp8_quantize_tile1x128(fake, fq.BF16, 4, 4, 2, 0, fake, None, fake, 0, None) == fq.EINVAL
     assert L.fp8_quantize_mx32(fake, fq.BF16, 4, 4, 0, 0, fake, None, None, 0, None) == fq.EINVAL
     assert L.fp8_quantize_block128x128(fake, fq.F32, -1, 4, 0, fake, None, fake, 0, None) == fq.EINVAL
+    # stochastic rounding: missing scale_out, small workspace
+    assert L.fp8_quantize_per_tensor_sr(fake, fq.BF16, 4, 4, 1, 1, 0, fake, None, None, None, 0, ws, 4096,
+                                        None) == fq.EINVAL
+    assert L.fp8_quantize_per_tensor_sr(fake, fq.BF16, 4, 4, 1, 1, 0, fake, None, fake, None, 0, ws, 16,
+                                        None) == fq.EWORKSPACE
     # rowwise: bad axis, missing scales, a transposed copy with axis 0
     assert L.fp8_quantize_rowwise(fake, fq.BF16, 4, 4, 2, 0, fake, None, fake, 0, None) == fq.EINVAL
     assert L.fp8_quantize_rowwise(fake, fq.BF16, 4, 4, 0, 0, fake, None, None, 0, None) == fq.EINVAL

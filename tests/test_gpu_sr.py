@@ -1,0 +1,63 @@
+"""GPU parity of the stochastically rounded cast (per-tensor current scaling,
+Philox4x32-10 words): codes bit-exact against the oracle for the same seed and
+offset, at small ragged shapes and at a full [15872, 4096] gradient."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_scaled_quantization_amax_amd as fq
+import oracle
+import workloads
+from gpu_util import announce, codes_equal, dev, host_input
+
+pytestmark = pytest.mark.gpu
+
+
+def check_sr(x, fmt, seed, offset, emit_t=False, saturate=False):
+    q, qT, s, a = fq.fp8_quantize_per_tensor_sr(x.to(dev()), fmt, seed, offset, emit_t=emit_t, saturate=saturate)
+    torch.cuda.synchronize()
+    oq, os_, oa = oracle.quantize_per_tensor_sr(host_input(x), fmt, seed, offset, saturate)
+    oq = oq.reshape(q.shape)
+    assert s.item() == os_ or (np.isnan(s.item()) and np.isnan(os_))
+    assert a.item() == oa or (np.isnan(a.item()) and np.isnan(oa))
+    assert codes_equal(q.cpu().numpy(), oq, fmt)
+    if emit_t:
+        assert codes_equal(qT.cpu().numpy(), oq.T, fmt)
+    return q
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (37, 53), (16, 4096), (129, 136), (1000, 24)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt", [fq.E5M2, fq.E4M3], ids=["e5m2", "e4m3"])
+def test_sr_bit_exact(shape, dtype, fmt):
+    announce("sr", shape, dtype, fmt)
+    x = workloads.normal(shape, 1.0, 9000 + shape[0] + shape[1], dtype)
+    check_sr(x, fmt, seed=0x0123456789ABCDEF, offset=(1 << 40) + 5, emit_t=shape[0] > 1)
+
+
+def test_sr_is_deterministic_and_offset_sensitive():
+    announce("sr determinism")
+    x = workloads.normal((256, 512), 1.0, 9100, torch.bfloat16).to(dev())
+    q1 = fq.fp8_quantize_per_tensor_sr(x, fq.E5M2, 7, 0)[0]
+    q2 = fq.fp8_quantize_per_tensor_sr(x, fq.E5M2, 7, 0)[0]
+    q3 = fq.fp8_quantize_per_tensor_sr(x, fq.E5M2, 7, 1)[0]
+    q4 = fq.fp8_quantize_per_tensor_sr(x, fq.E5M2, 8, 0)[0]
+    assert torch.equal(q1, q2)
+    assert not torch.equal(q1, q3) and not torch.equal(q1, q4)
+
+
+def test_sr_saturate_and_nan():
+    announce("sr saturate / nan")
+    x = workloads.normal((64, 96), 1.0, 9200, torch.float32)
+    check_sr(x, fq.E4M3, 3, 4, saturate=True)
+    x[7, 9] = float("nan")
+    check_sr(x, fq.E5M2, 3, 4)
+
+
+def test_sr_full_size_gradient():
+    """A gradient-shaped tensor at full size: bf16 [15872, 4096] ~ N(0,1), E5M2,
+    with the K-major copy a wgrad operand needs."""
+    announce("sr full size")
+    g = workloads.normal((workloads.M_TOKENS, workloads.HIDDEN), 1.0, 9300, torch.bfloat16)
+    check_sr(g, fq.E5M2, seed=2024, offset=17, emit_t=True)

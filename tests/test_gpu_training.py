@@ -154,3 +154,39 @@ def test_rowwise_training_parity(training, lab):
     assert gap < 0.10
     assert rel[0] <= TOL_F32
     assert rel.max() < 0.05
+
+
+def test_sr_gradient_one_step_matches_oracle(training, lab):
+    """Stochastically rounded output gradient (same seed and offset on both
+    sides, so the same codes): forward output and both gradients agree with
+    the oracle."""
+    dev = torch.device("cuda")
+    h = torch.relu(lab["X"] @ lab["W1"].T)
+    g = torch.randn(512, 16, generator=torch.Generator().manual_seed(8)) * 1e-3
+    xo, wo = h.clone().requires_grad_(), lab["W2"].clone().requires_grad_()
+    yo = fp8_train.OracleFP8Matmul.apply(xo, wo, (99, 5))
+    yo.backward(g)
+    xg, wg = h.to(dev).requires_grad_(), lab["W2"].to(dev).requires_grad_()
+    yg = training.fp8_matmul(xg, wg, sr=(99, 5))
+    yg.backward(g.to(dev))
+    torch.cuda.synchronize()
+    _close(yg, yo, "y")
+    _close(xg.grad, xo.grad, "dx")
+    _close(wg.grad, wo.grad, "dw")
+
+
+def test_sr_gradient_training_parity(training, lab):
+    """Check [5]'s bound on the GPU with stochastically rounded gradients, and
+    the loss curve against the oracle's run with the same seed."""
+    dev = torch.device("cuda")
+    X, Y, W1, W2 = (lab[k].to(dev) for k in ("X", "Y", "W1", "W2"))
+    ls = training.train_mlp(X, Y, W1, W2, fp8=True, grad_sr_seed=1234)
+    l32 = training.train_mlp(X, Y, W1, W2, fp8=False)
+    os_ = fp8_train.train_mlp(lab["X"], lab["Y"], lab["W1"], lab["W2"], fp8=True, grad_sr_seed=1234)
+    gap = abs(ls[-1] - l32[-1]) / l32[-1]
+    rel = np.abs(np.array(ls) - np.array(os_)) / np.array(os_)
+    print(f"SR gradients: final loss fp32 {l32[-1]:.6f}, FP8 GPU {ls[-1]:.6f}, FP8 oracle {os_[-1]:.6f}; gap "
+          f"{100 * gap:.2f}%; GPU vs oracle step 0 {rel[0]:.2e}, all {rel.max():.2e}", flush=True)
+    assert gap < 0.10
+    assert rel[0] <= TOL_F32
+    assert rel.max() < 0.05

@@ -97,3 +97,12 @@ def test_rowwise_lab_check5_final_loss_gap():
     lr = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=True, recipe="rowwise")
     assert abs(lr[-1] - l32[-1]) / l32[-1] < 0.10
     assert lr[-1] < 0.5 * lr[0]
+
+
+def test_sr_gradients_lab_check5_final_loss_gap():
+    """Check [5]'s bound with stochastically rounded E5M2 gradients."""
+    d = workloads.lab_mlp_inputs()
+    l32 = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=False)
+    ls = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=True, grad_sr_seed=1234)
+    assert abs(ls[-1] - l32[-1]) / l32[-1] < 0.10
+    assert ls[-1] < 0.5 * ls[0]

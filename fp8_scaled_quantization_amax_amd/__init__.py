@@ -67,6 +67,7 @@ def lib():
             "fp8_quantize_rowwise": (I, [P, I, I64, I64, I, I, P, P, P, U, P]),
             "fp8_quantize_per_tensor_sr": (I, [P, I, I64, I64, I, ctypes.c_uint64, ctypes.c_uint64, P, P, P, P, U, P,
                                                SZ, P]),
+            "fp8_quantize_per_tensor_rht": (I, [P, I, I64, I64, I, ctypes.c_uint64, P, P, P, P, U, P, SZ, P]),
             "fp8_gemm_workspace_bytes": (SZ, [I, I64, I64, I64, OP, OP]),
             "fp8_gemm_scaled_NT": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
             "fp8_gemm_scaled_NN": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
@@ -184,6 +185,22 @@ def fp8_quantize_per_tensor_sr(x, fmt=E5M2, seed=0, offset=0, emit_t=False, satu
     _check(lib().fp8_quantize_per_tensor_sr(_ptr(x), hp, rows, cols, fmt, int(seed) & (2 ** 64 - 1),
                                             int(offset) & (2 ** 64 - 1), _ptr(q), _ptr(qT), _ptr(scale), _ptr(amax),
                                             SATURATE if saturate else 0, _ptr(ws), ws.numel(), _stream()))
+    return q, qT, scale, amax
+
+
+def fp8_quantize_per_tensor_rht(x, fmt=E4M3, seed=0, emit_t=False, saturate=False, ws=None):
+    """Random Hadamard transform along rows (16-row blocks, signs from seed),
+    then per-tensor current quantization; returns (q, qT, scale, amax)."""
+    hp = _hp(x)
+    rows, cols = _rows_cols(x)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if emit_t else None
+    scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = reduce_workspace(x.device) if ws is None else ws
+    _check(lib().fp8_quantize_per_tensor_rht(_ptr(x), hp, rows, cols, fmt, int(seed) & (2 ** 64 - 1), _ptr(q),
+                                             _ptr(qT), _ptr(scale), _ptr(amax), SATURATE if saturate else 0, _ptr(ws),
+                                             ws.numel(), _stream()))
     return q, qT, scale, amax
 
 

@@ -423,6 +423,28 @@ int fp8_quantize_per_tensor_sr(const void* x, int hp, int64_t rows, int64_t cols
     return ok();
 }
 
+int fp8_quantize_per_tensor_rht(const void* x, int hp, int64_t rows, int64_t cols, int fmt, uint64_t seed,
+                                uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out, unsigned flags, void* ws,
+                                size_t ws_bytes, void* stream) {
+    int r;
+    if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags)) != FP8Q_OK) return r;
+    if (scale_out == nullptr) return fail(FP8Q_EINVAL, "scale_out is required");
+    if (rows % 16 != 0 || cols % 8 != 0)
+        return fail(FP8Q_EALIGN, "rows=%lld must be a multiple of 16 and cols=%lld of 8", (long long)rows,
+                    (long long)cols);
+    if ((uintptr_t)x % 16 != 0 || (uintptr_t)q % 8 != 0)
+        return fail(FP8Q_EALIGN, "x must be 16-byte and q 8-byte aligned");
+    if (ws == nullptr || ws_bytes < fp8q::kReduceWsBytes)
+        return fail(FP8Q_EWORKSPACE, "reduce workspace of %zu bytes needed", fp8q::kReduceWsBytes);
+    if ((r = check_device()) != FP8Q_OK) return r;
+    if ((r = launched(fp8q::launch_quantize_rht(x, hp, rows, cols, fmt, (flags & FP8Q_SATURATE) != 0, seed,
+                                                reinterpret_cast<float*>(ws), q, qT, scale_out, amax_out,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                      "quantize")) != FP8Q_OK)
+        return r;
+    return ok();
+}
+
 int fp8_quantize_tile1x128(const void* x, int hp, int64_t rows, int64_t cols, int axis, int fmt, uint8_t* q,
                            uint8_t* qT, float* scales, unsigned flags, void* stream) {
     int r;

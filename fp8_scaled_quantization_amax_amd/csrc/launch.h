@@ -77,6 +77,14 @@ hipError_t launch_quantize_sr(const void* x, int hp, int64_t n, int fmt, bool sa
                               const float* partials, int nparts, uint8_t* q, float* scale_out, float* amax_out,
                               hipStream_t s);
 
+// Random Hadamard transform along rows (16-row blocks, signs from Philox with
+// key seed) fused with per-tensor current quantization of the result;
+// rows % 16 == 0, cols % 8 == 0, x 16-byte and q 8-byte aligned.  partials:
+// the reduce workspace's partial maxima (kReduceParts floats).
+hipError_t launch_quantize_rht(const void* x, int hp, int64_t rows, int64_t cols, int fmt, bool sat, uint64_t seed,
+                               float* partials, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
+                               hipStream_t s);
+
 // Rowwise quantization: one fp32 scale per row (axis 0) or per column (axis
 // 1) into scales, codes into q [rows, cols], and (if qT != NULL) their
 // transpose into qT [cols, rows].  Axis 1 keeps integer maxima in `scales`

@@ -21,7 +21,8 @@ targets, loss and AdamW are plain torch ops around them.
 import torch
 
 from . import (E4M3, E5M2, ROWWISE, GemmOperand, fp8_gemm_scaled_NN, fp8_gemm_scaled_NT, fp8_gemm_scaled_TN,
-               fp8_quantize_per_tensor, fp8_quantize_per_tensor_sr, fp8_quantize_rowwise)
+               fp8_quantize_per_tensor, fp8_quantize_per_tensor_rht, fp8_quantize_per_tensor_sr,
+               fp8_quantize_rowwise)
 
 
 class FP8Matmul(torch.autograd.Function):
@@ -30,10 +31,13 @@ class FP8Matmul(torch.autograd.Function):
     x and w are fp32 or bf16 (the same dtype); y, dx and dw come out in that
     dtype (fp32 accumulation, one rounding at the end).  With sr = (seed,
     offset) the output gradient is rounded stochastically
-    (fp8_quantize_per_tensor_sr) instead of to nearest."""
+    (fp8_quantize_per_tensor_sr) instead of to nearest.  With rht = seed the
+    wgrad GEMM takes dy and x through the random Hadamard transform along the
+    tokens (fp8_quantize_per_tensor_rht, one seed for both), which leaves
+    dy^T x unchanged and spreads outlier tokens before quantization."""
 
     @staticmethod
-    def forward(ctx, x, w, sr=None):
+    def forward(ctx, x, w, sr=None, rht=None):
         if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
             raise ValueError(f"FP8Matmul needs x[M,K] and w[N,K], got {tuple(x.shape)} and {tuple(w.shape)}")
         if x.dtype != w.dtype or x.dtype not in (torch.float32, torch.bfloat16):
@@ -43,17 +47,17 @@ class FP8Matmul(torch.autograd.Function):
         N = w.shape[0]
         # K-major copies only for the backward GEMMs that will run: x's for
         # wgrad, w's for dgrad (none in forward-only use)
-        qx, qxT, sx, _ = fp8_quantize_per_tensor(x, E4M3, emit_t=ctx.needs_input_grad[1])
+        qx, qxT, sx, _ = fp8_quantize_per_tensor(x, E4M3, emit_t=ctx.needs_input_grad[1] and rht is None)
         qw, qwT, sw, _ = fp8_quantize_per_tensor(w, E4M3, emit_t=ctx.needs_input_grad[0])
         y = fp8_gemm_scaled_NT(M, N, K, GemmOperand.quantized(qx, E4M3, sx),
                                GemmOperand.quantized(qw, E4M3, sw), x.dtype)
-        ctx.save_for_backward(qx, qxT, sx, qw, qwT, sw)
-        ctx.dtype, ctx.sr = x.dtype, sr
+        ctx.save_for_backward(qx, qxT, sx, qw, qwT, sw, x if rht is not None and ctx.needs_input_grad[1] else None)
+        ctx.dtype, ctx.sr, ctx.rht = x.dtype, sr, rht
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        qx, qxT, sx, qw, qwT, sw = ctx.saved_tensors
+        qx, qxT, sx, qw, qwT, sw, x_hp = ctx.saved_tensors
         dy = dy.to(ctx.dtype).contiguous()
         M, N = dy.shape
         K = qx.shape[1]
@@ -65,10 +69,15 @@ class FP8Matmul(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             dx = fp8_gemm_scaled_NN(M, K, N, GemmOperand.quantized(qg, E5M2, sg),
                                     GemmOperand.quantized(qw, E4M3, sw, kmajor=qwT), ctx.dtype)
-        if ctx.needs_input_grad[1]:
+        if ctx.needs_input_grad[1] and ctx.rht is not None:
+            hg, hgT, shg, _ = fp8_quantize_per_tensor_rht(dy, E5M2, ctx.rht, emit_t=True)
+            hx, hxT, shx, _ = fp8_quantize_per_tensor_rht(x_hp, E4M3, ctx.rht, emit_t=True)
+            dw = fp8_gemm_scaled_TN(N, K, M, GemmOperand.quantized(hg, E5M2, shg, kmajor=hgT),
+                                    GemmOperand.quantized(hx, E4M3, shx, kmajor=hxT), ctx.dtype)
+        elif ctx.needs_input_grad[1]:
             dw = fp8_gemm_scaled_TN(N, K, M, GemmOperand.quantized(qg, E5M2, sg, kmajor=qgT),
                                     GemmOperand.quantized(qx, E4M3, sx, kmajor=qxT), ctx.dtype)
-        return dx, dw, None
+        return dx, dw, None, None
 
 
 class FP8MatmulRowwise(torch.autograd.Function):
@@ -126,23 +135,26 @@ class FP8MatmulRowwise(torch.autograd.Function):
         return dx, dw
 
 
-def fp8_matmul(x, w, recipe="tensorwise", sr=None):
+def fp8_matmul(x, w, recipe="tensorwise", sr=None, rht=None):
     """x . w^T through FP8Matmul ("tensorwise", optionally with stochastically
-    rounded gradients: sr = (seed, offset)) or FP8MatmulRowwise ("rowwise")."""
+    rounded gradients, sr = (seed, offset), and a Hadamard-transformed wgrad,
+    rht = seed) or FP8MatmulRowwise ("rowwise")."""
     if recipe == "rowwise":
-        if sr is not None:
-            raise ValueError("stochastic rounding is implemented for the tensorwise recipe")
+        if sr is not None or rht is not None:
+            raise ValueError("stochastic rounding and the Hadamard transform are implemented for the tensorwise recipe")
         return FP8MatmulRowwise.apply(x, w)
     if recipe != "tensorwise":
         raise ValueError(f"unknown recipe {recipe!r}")
-    return FP8Matmul.apply(x, w, sr)
+    return FP8Matmul.apply(x, w, sr, rht)
 
 
-def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None):
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None,
+              wgrad_rht_seed=None):
     """The lab page's check-[5] loop: the 2-layer MLP relu(X W1^T) W2^T is fitted
     to Y by mean squared error with AdamW(lr), with every matmul either FP8
     (`fp8_matmul` with `recipe`; with grad_sr_seed, output gradients rounded
-    stochastically, offset 2 step + layer) or plain fp32.  X, Y, W1 and W2 are device tensors; the
+    stochastically, offset 2 step + layer; with wgrad_rht_seed, Hadamard-transformed
+    wgrad operands, seed wgrad_rht_seed + 2 step + layer) or plain fp32.  X, Y, W1 and W2 are device tensors; the
     weights are copied and left unchanged.  Returns the list of per-step
     losses (floats, read once at the end)."""
     W1 = W1.detach().clone().requires_grad_()
@@ -151,7 +163,8 @@ def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", g
     def mm(a, b, t, j):
         if not fp8:
             return a @ b.T
-        return fp8_matmul(a, b, recipe, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j))
+        return fp8_matmul(a, b, recipe, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j),
+                          None if wgrad_rht_seed is None else wgrad_rht_seed + 2 * t + j)
     losses = []
     for t in range(steps):
         loss = ((mm(torch.relu(mm(X, W1, t, 0)), W2, t, 1) - Y) ** 2).mean()

@@ -181,6 +181,32 @@ int fp8_quantize_per_tensor_sr(const void* x, int hp, int64_t rows, int64_t cols
                                unsigned flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Random Hadamard transform along the rows (the token axis of a wgrad operand;
+ * "How to Optimize Transformer-Based Models for Low-Precision Training" lists
+ * random Hadamard transforms on the wgrad inputs in its recipe) fused with
+ * per-tensor current quantization of the result.
+ * y = R x with R block-diagonal over 16-row blocks, each block
+ * (1/4) H16 diag(d): H16 the Sylvester Hadamard matrix, H16[i][j] =
+ * (-1)^popcount(i & j); d_t = -1 when the top bit of word t mod 4 of
+ * Philox4x32-10(counter (low, high 32 bits of t / 4, 0, 0), key (low, high
+ * 32 bits of seed)) is set, else +1.  R is orthogonal, so two wgrad operands
+ * transformed with the same seed give the same product: (R G)^T (R X) = G^T X.
+ * y is computed in fp32 in this order: signs, then the butterflies
+ * (a + b, a - b) with partners 1, 2, 4, 8 rows apart, then times 1/4.
+ * y is then quantized like fp8_quantize_per_tensor with current scaling:
+ * s = max(amax(y) / fmax, 1e-12), q = RNE_fp8(RN_fp32(y / s)).  y itself is
+ * not stored.
+ * Needs rows % 16 == 0 and cols % 8 == 0, x 16-byte and q 8-byte aligned
+ * (else FP8Q_EALIGN).  q [rows, cols] is required; qT [cols, rows] is
+ * optional (the K-major copy for fp8_gemm_scaled_TN).  ws: the reduce
+ * workspace.  Other errors as fp8_quantize_per_tensor.
+ */
+int fp8_quantize_per_tensor_rht(const void* x, int hp, int64_t rows, int64_t cols, int fmt,
+                                uint64_t seed, uint8_t* q, uint8_t* qT, float* scale_out,
+                                float* amax_out, unsigned flags, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * 1x128 tile quantization with fp32 scales (lab page smoke check [4]).
  *   axis = 0: tiles of 128 consecutive columns of a row;
  *             scales [rows, ceil(cols/128)].

@@ -60,6 +60,8 @@ def lib():
         L.orc_encode_sr.restype, L.orc_encode_sr.argtypes = ctypes.c_uint8, [F, U32, I32, I32]
         L.orc_quantize_per_tensor_sr.restype = None
         L.orc_quantize_per_tensor_sr.argtypes = [P, I32, I64, I32, I32, U64, U64, P, P, P]
+        L.orc_rht_sign.restype, L.orc_rht_sign.argtypes = I32, [U64, I64]
+        L.orc_rht.restype, L.orc_rht.argtypes = None, [P, I32, I64, I64, U64, P]
         L.orc_encode_compare_range.restype = I64
         L.orc_encode_compare_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, P,
                                                ctypes.POINTER(ctypes.c_uint64)]
@@ -169,6 +171,25 @@ def quantize_per_tensor_sr(x, fmt, seed, offset=0, saturate=False):
     lib().orc_quantize_per_tensor_sr(_ptr(x), hp, x.size, fmt, int(saturate), int(seed), int(offset), _ptr(q),
                                      _ptr(s), _ptr(a))
     return q, s[0], a[0]
+
+
+def rht_sign(seed, t):
+    return int(lib().orc_rht_sign(int(seed), int(t)))
+
+
+def rht(x, seed):
+    """Random Hadamard transform along rows (16-row blocks): fp32 [rows, cols]."""
+    x, hp = _hp(x)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), np.float32)
+    lib().orc_rht(_ptr(x), hp, rows, cols, int(seed), _ptr(y))
+    return y
+
+
+def quantize_per_tensor_rht(x, fmt, seed, saturate=False):
+    """The transform, then per-tensor current quantization of its fp32 result:
+    (codes, scale, amax of the transformed tensor)."""
+    return quantize_per_tensor(rht(x, seed), fmt, saturate)
 
 
 class DelayedState:

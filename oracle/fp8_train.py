@@ -16,7 +16,8 @@ loop on the CPU.
 import numpy as np
 import torch
 
-from . import E4M3, E5M2, Scale, gemm_nn, gemm_nt, gemm_tn, quantize_per_tensor, quantize_per_tensor_sr, quantize_rowwise
+from . import (E4M3, E5M2, Scale, gemm_nn, gemm_nt, gemm_tn, quantize_per_tensor, quantize_per_tensor_rht,
+               quantize_per_tensor_sr, quantize_rowwise)
 
 
 def _q(t, fmt):
@@ -26,27 +27,34 @@ def _q(t, fmt):
 
 class OracleFP8Matmul(torch.autograd.Function):
     """y = x . w^T with E4M3 inputs forward and an E5M2 output gradient backward
-    (rounded stochastically with sr = (seed, offset))."""
+    (rounded stochastically with sr = (seed, offset)); with rht = seed, the
+    wgrad operands dy and x go through the random Hadamard transform first."""
 
     @staticmethod
-    def forward(ctx, x, w, sr=None):
+    def forward(ctx, x, w, sr=None, rht=None):
         qx, sx = _q(x, E4M3)
         qw, sw = _q(w, E4M3)
-        ctx.saved = (qx, sx, qw, sw)
-        ctx.sr = sr
+        ctx.saved = (qx, sx, qw, sw, x.detach().clone())
+        ctx.sr, ctx.rht = sr, rht
         return torch.from_numpy(gemm_nt(qx, qw, E4M3, E4M3, sx, sw).astype(np.float32))
 
     @staticmethod
     def backward(ctx, dy):
-        qx, sx, qw, sw = ctx.saved
+        qx, sx, qw, sw, x = ctx.saved
         if ctx.sr is None:
             qg, sg = _q(dy, E5M2)
         else:
             qg, s, _ = quantize_per_tensor_sr(dy.detach().contiguous().numpy(), E5M2, ctx.sr[0], ctx.sr[1])
             sg = Scale("tensor", s)
         dx = torch.from_numpy(gemm_nn(qg, qw, E5M2, E4M3, sg, sw).astype(np.float32))
-        dw = torch.from_numpy(gemm_tn(qg, qx, E5M2, E4M3, sg, sx).astype(np.float32))
-        return dx, dw, None
+        if ctx.rht is None:
+            dw = torch.from_numpy(gemm_tn(qg, qx, E5M2, E4M3, sg, sx).astype(np.float32))
+        else:
+            hg, shg, _ = quantize_per_tensor_rht(dy.detach().contiguous().numpy(), E5M2, ctx.rht)
+            hx, shx, _ = quantize_per_tensor_rht(x.contiguous().numpy(), E4M3, ctx.rht)
+            dw = torch.from_numpy(gemm_tn(hg, hx, E5M2, E4M3, Scale("tensor", shg), Scale("tensor", shx))
+                                  .astype(np.float32))
+        return dx, dw, None, None
 
 
 def _qr(t, fmt, axis, K):
@@ -82,7 +90,8 @@ class OracleFP8MatmulRowwise(torch.autograd.Function):
         return dx, dw
 
 
-def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None):
+def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None,
+              wgrad_rht_seed=None):
     """Fit relu(X W1^T) W2^T to Y by mean squared error with AdamW(lr), every
     matmul either the oracle's FP8 matmul of `recipe` or plain fp32; returns
     the per-step losses."""
@@ -94,7 +103,8 @@ def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", g
             return a @ b.T
         if recipe == "rowwise":
             return OracleFP8MatmulRowwise.apply(a, b)
-        return OracleFP8Matmul.apply(a, b, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j))
+        return OracleFP8Matmul.apply(a, b, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j),
+                                     None if wgrad_rht_seed is None else wgrad_rht_seed + 2 * t + j)
     losses = []
     for t in range(steps):
         loss = ((mm(torch.relu(mm(X, W1, t, 0)), W2, t, 1) - Y) ** 2).mean()

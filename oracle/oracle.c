@@ -312,6 +312,49 @@ void orc_quantize_per_tensor_sr(const void* x, int hp, int64_t n, int fmt, int s
 }
 
 /* ------------------------------------------------------------------ */
+/* Random Hadamard transform of a wgrad operand ([BLOG] lists random      */
+/* Hadamard transforms on the wgrad inputs among its recipe's extra       */
+/* operations; the form below is a reading, listed in the design notes). */
+/* ------------------------------------------------------------------ */
+
+/* Sign of token t: -1 when the top bit of its Philox word (offset 0) is set. */
+int orc_rht_sign(uint64_t seed, int64_t t)
+{
+    return (orc_sr_word(seed, 0, (uint64_t)t) >> 31) ? -1 : 1;
+}
+
+/* y = R x along rows, R = blockdiag over 16-row blocks of (1/4) H16 diag(d):
+ * in fp32, signs first, then the Walsh-Hadamard butterflies (a + b, a - b)
+ * with partners 1, 2, 4, 8 rows apart (which multiply by the Sylvester H16,
+ * H16[i][j] = (-1)^popcount(i & j)), then the factor 1/4.  rows % 16 == 0. */
+void orc_rht(const void* x, int hp, int64_t rows, int64_t cols, uint64_t seed, float* y)
+{
+    const int64_t nb = rows / 16;
+    int64_t b;
+#pragma omp parallel for schedule(static)
+    for (b = 0; b < nb; ++b) {
+        int sg[16], i, h;
+        int64_t c;
+        for (i = 0; i < 16; ++i) sg[i] = orc_rht_sign(seed, b * 16 + i);
+        for (c = 0; c < cols; ++c) {
+            float v[16];
+            for (i = 0; i < 16; ++i) {
+                v[i] = load_hp(x, hp, (b * 16 + i) * cols + c);
+                if (sg[i] < 0) v[i] = -v[i];
+            }
+            for (h = 1; h < 16; h <<= 1)
+                for (i = 0; i < 16; ++i)
+                    if ((i & h) == 0) {
+                        const float a = v[i], d = v[i + h];
+                        v[i] = a + d;
+                        v[i + h] = a - d;
+                    }
+            for (i = 0; i < 16; ++i) y[(b * 16 + i) * cols + c] = v[i] * 0.25f;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Granular scaling: 1 x T tiles ([LAB] check [4]: scaled_roundtrip per   */
 /* 128-wide row), T x 1 tiles, Br x Bc blocks ([SJ] "block"; [BLOG] 2D    */
 /* block scaling for weights), MX blocks of 32 with an E8M0 power-of-two  */

@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fp8_amax", "fp8_quantize_per_tensor", "fp8_quantize_tile1x128", "fp8_quantize_block128x128",
-              "fp8_quantize_mx32", "fp8_quantize_rowwise", "fp8_quantize_per_tensor_sr", "fp8_gemm_scaled_NT", "fp8_gemm_scaled_NN", "fp8_gemm_scaled_TN",
+              "fp8_quantize_mx32", "fp8_quantize_rowwise", "fp8_quantize_per_tensor_sr",
+              "fp8_quantize_per_tensor_rht", "fp8_gemm_scaled_NT", "fp8_gemm_scaled_NN", "fp8_gemm_scaled_TN",
               "fp8_gemm_workspace_bytes", "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version",
               "fp8q_reduce_workspace_bytes"):
         assert n in names
@@ -78,6 +79,13 @@ def test_invalid_arguments_are_rejected_before_any_gpu_call():
                                         None) == fq.EINVAL
     assert L.fp8_quantize_per_tensor_sr(fake, fq.BF16, 4, 4, 1, 1, 0, fake, None, fake, None, 0, ws, 16,
                                         None) == fq.EWORKSPACE
+    # Hadamard: rows not a multiple of 16, cols not of 8, misaligned x
+    assert L.fp8_quantize_per_tensor_rht(fake, fq.BF16, 24, 16, 0, 1, fake, None, fake, None, 0, ws, 4096,
+                                         None) == fq.EALIGN
+    assert L.fp8_quantize_per_tensor_rht(fake, fq.BF16, 32, 12, 0, 1, fake, None, fake, None, 0, ws, 4096,
+                                         None) == fq.EALIGN
+    assert L.fp8_quantize_per_tensor_rht(P(0x10008), fq.BF16, 32, 16, 0, 1, fake, None, fake, None, 0, ws, 4096,
+                                         None) == fq.EALIGN
     # rowwise: bad axis, missing scales, a transposed copy with axis 0
     assert L.fp8_quantize_rowwise(fake, fq.BF16, 4, 4, 2, 0, fake, None, fake, 0, None) == fq.EINVAL
     assert L.fp8_quantize_rowwise(fake, fq.BF16, 4, 4, 0, 0, fake, None, None, 0, None) == fq.EINVAL

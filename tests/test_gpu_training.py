@@ -190,3 +190,38 @@ def test_sr_gradient_training_parity(training, lab):
     assert gap < 0.10
     assert rel[0] <= TOL_F32
     assert rel.max() < 0.05
+
+
+def test_rht_wgrad_one_step_matches_oracle(training, lab):
+    """Hadamard-transformed wgrad operands (same seed on both sides): forward
+    output and both gradients agree with the oracle."""
+    dev = torch.device("cuda")
+    h = torch.relu(lab["X"] @ lab["W1"].T)
+    g = torch.randn(512, 16, generator=torch.Generator().manual_seed(9)) * 1e-3
+    xo, wo = h.clone().requires_grad_(), lab["W2"].clone().requires_grad_()
+    yo = fp8_train.OracleFP8Matmul.apply(xo, wo, None, 321)
+    yo.backward(g)
+    xg, wg = h.to(dev).requires_grad_(), lab["W2"].to(dev).requires_grad_()
+    yg = training.fp8_matmul(xg, wg, rht=321)
+    yg.backward(g.to(dev))
+    torch.cuda.synchronize()
+    _close(yg, yo, "y")
+    _close(xg.grad, xo.grad, "dx")
+    _close(wg.grad, wo.grad, "dw")
+
+
+def test_rht_wgrad_training_parity(training, lab):
+    """Check [5]'s bound on the GPU with Hadamard-transformed wgrad operands,
+    and the loss curve against the oracle's run with the same seeds."""
+    dev = torch.device("cuda")
+    X, Y, W1, W2 = (lab[k].to(dev) for k in ("X", "Y", "W1", "W2"))
+    lh = training.train_mlp(X, Y, W1, W2, fp8=True, wgrad_rht_seed=500)
+    l32 = training.train_mlp(X, Y, W1, W2, fp8=False)
+    oh = fp8_train.train_mlp(lab["X"], lab["Y"], lab["W1"], lab["W2"], fp8=True, wgrad_rht_seed=500)
+    gap = abs(lh[-1] - l32[-1]) / l32[-1]
+    rel = np.abs(np.array(lh) - np.array(oh)) / np.array(oh)
+    print(f"RHT wgrad: final loss fp32 {l32[-1]:.6f}, FP8 GPU {lh[-1]:.6f}, FP8 oracle {oh[-1]:.6f}; gap "
+          f"{100 * gap:.2f}%; GPU vs oracle step 0 {rel[0]:.2e}, all {rel.max():.2e}", flush=True)
+    assert gap < 0.10
+    assert rel[0] <= TOL_F32
+    assert rel.max() < 0.05

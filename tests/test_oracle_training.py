@@ -106,3 +106,12 @@ def test_sr_gradients_lab_check5_final_loss_gap():
     ls = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=True, grad_sr_seed=1234)
     assert abs(ls[-1] - l32[-1]) / l32[-1] < 0.10
     assert ls[-1] < 0.5 * ls[0]
+
+
+def test_rht_wgrad_lab_check5_final_loss_gap():
+    """Check [5]'s bound with Hadamard-transformed wgrad operands."""
+    d = workloads.lab_mlp_inputs()
+    l32 = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=False)
+    lh = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=True, wgrad_rht_seed=500)
+    assert abs(lh[-1] - l32[-1]) / l32[-1] < 0.10
+    assert lh[-1] < 0.5 * lh[0]

@@ -162,6 +162,29 @@ __device__ __forceinline__ float e8m0_recip(int code) {
     return __uint_as_float((uint32_t)(254 - code) << 23);
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC 2011): ten rounds of (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
+// with (hi0, lo0) = 0xD2511F53 * c0 and (hi1, lo1) = 0xCD9E8D57 * c2 as full
+// 64-bit products (one multiply-add instruction each); the key gains
+// 0x9E3779B9 and 0xBB67AE85 before each round after the first.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0;
+        c1 = (uint32_t)p1;
+        c2 = n2;
+        c3 = (uint32_t)p0;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
 // bf16 round to nearest even of an fp32 value (NaN kept quiet).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     const uint32_t b = __float_as_uint(f);

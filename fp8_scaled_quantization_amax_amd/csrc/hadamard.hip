@@ -18,9 +18,10 @@
 // cast quantizes x: amax over y, s = max(amax / fmax, 1e-12), q = fp8(RN32(y / s)).
 //
 // Design: the amax of y needs all of y first, so the transform runs twice
-// from x (it is cheap next to the memory traffic) instead of writing y out:
-// pass 1 takes each block's max |y| as a partial maximum, pass 2 folds the
-// partials into the scale and casts.  A thread owns one 16-row block of 8
+// from x instead of writing y out and reading it back (2 x 4 bytes per element
+// more HBM traffic): pass 1 takes each block's max |y| as a partial maximum,
+// pass 2 folds the partials into the scale and casts.  With the butterflies,
+// the divisions and the sign draws done twice, the pair is ALU-bound.  A thread owns one 16-row block of 8
 // columns: 16 loads of 16 bytes (bf16) from consecutive rows, 8 transforms of
 // 16 values in registers, 16 stores of 8 codes; neighbouring threads take
 // neighbouring column groups, so every load and store is coalesced.
@@ -31,32 +32,13 @@
 
 namespace fp8q {
 
-__device__ __forceinline__ uint4 philox_rht(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
-                                            uint32_t k1) {
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r > 0) {
-            k0 += 0x9E3779B9u;
-            k1 += 0xBB67AE85u;
-        }
-        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
-        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-        c0 = n0;
-        c1 = lo1;
-        c2 = n2;
-        c3 = lo0;
-    }
-    return make_uint4(c0, c1, c2, c3);
-}
-
 // Sign bits of the 16 tokens of block b (bit i set: token 16 b + i negated).
 __device__ __forceinline__ uint32_t rht_signs(int64_t b, uint32_t k0, uint32_t k1) {
     uint32_t bits = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint64_t g = (uint64_t)b * 4 + q;   // tokens 16 b + 4 q .. + 3
-        const uint4 w = philox_rht((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, k0, k1);
+        const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, k0, k1);
         bits |= ((w.x >> 31) << (4 * q)) | ((w.y >> 31) << (4 * q + 1)) | ((w.z >> 31) << (4 * q + 2)) |
                 ((w.w >> 31) << (4 * q + 3));
     }

@@ -162,6 +162,15 @@ __device__ __forceinline__ float e8m0_recip(int code) {
     return __uint_as_float((uint32_t)(254 - code) << 23);
 }
 
+// 16-byte load with the non-temporal hint, for inputs a pass reads once:
+// keeping them in the caches would only evict other data (measured: the amax
+// pass over 130 MB of bf16 went from 26.7 to 22.9 us with it).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
 // as 1, 2, 3", SC 2011): ten rounds of (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
 // with (hi0, lo0) = 0xD2511F53 * c0 and (hi1, lo1) = 0xCD9E8D57 * c2 as full

@@ -53,7 +53,7 @@ __device__ __forceinline__ void rht_block(const void* __restrict__ x, int64_t co
     for (int i = 0; i < 16; ++i) {
         const int64_t off = (b * 16 + i) * cols + c0;
         if constexpr (HP == FP8Q_BF16) {
-            const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
+            const uint4 w = load_stream16(reinterpret_cast<const uint16_t*>(x) + off);
             const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -61,10 +61,12 @@ __device__ __forceinline__ void rht_block(const void* __restrict__ x, int64_t co
                 y[i][2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
             }
         } else {
-            const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
-            const float4 a = p[0], c = p[1];
-            y[i][0] = a.x; y[i][1] = a.y; y[i][2] = a.z; y[i][3] = a.w;
-            y[i][4] = c.x; y[i][5] = c.y; y[i][6] = c.z; y[i][7] = c.w;
+            const float* p = reinterpret_cast<const float*>(x) + off;
+            const uint4 a = load_stream16(p), c = load_stream16(p + 4);
+            y[i][0] = __uint_as_float(a.x); y[i][1] = __uint_as_float(a.y);
+            y[i][2] = __uint_as_float(a.z); y[i][3] = __uint_as_float(a.w);
+            y[i][4] = __uint_as_float(c.x); y[i][5] = __uint_as_float(c.y);
+            y[i][6] = __uint_as_float(c.z); y[i][7] = __uint_as_float(c.w);
         }
         if ((signs >> i) & 1u) {
 #pragma unroll

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restri
             for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * 8) {
                 uint4 w[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) w[u] = i + u * 256 < b1 ? xv[i + u * 256] : make_uint4(0, 0, 0, 0);
+                for (int u = 0; u < 8; ++u) w[u] = i + u * 256 < b1 ? load_stream16(xv + i + u * 256) : make_uint4(0, 0, 0, 0);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t d[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restri
             for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * 8) {
                 uint4 w[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) w[u] = i + u * 256 < b1 ? xv[i + u * 256] : make_uint4(0, 0, 0, 0);
+                for (int u = 0; u < 8; ++u) w[u] = i + u * 256 < b1 ? load_stream16(xv + i + u * 256) : make_uint4(0, 0, 0, 0);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t d[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
@@ -236,7 +236,7 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t rows, 
                                       int64_t col, bool vec, float v[8]) {
     if (row < rows && vec && col + 8 <= cols) {
         if constexpr (HP == FP8Q_BF16) {
-            const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + row * cols + col);
+            const uint4 w = load_stream16(reinterpret_cast<const uint16_t*>(x) + row * cols + col);
             const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -244,10 +244,12 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t rows, 
                 v[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
             }
         } else {
-            const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + row * cols + col);
-            const float4 a = p[0], b = p[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            const float* p = reinterpret_cast<const float*>(x) + row * cols + col;
+            const uint4 a = load_stream16(p), b = load_stream16(p + 4);
+            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+            v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+            v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+            v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
         }
     } else {
 #pragma unroll
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
             uint4 w = make_uint4(0, 0, 0, 0);
             if (row < rows && col < cols) {
                 if (vec_in && col + 16 <= cols) {
-                    w = *reinterpret_cast<const uint4*>(in + row * cols + col);
+                    w = load_stream16(in + row * cols + col);
                 } else {
                     uint32_t d[4] = {0, 0, 0, 0};
                     for (int e = 0; e < 16 && col + e < cols; ++e) d[e >> 2] |= (uint32_t)in[row * cols + col + e] << (8 * (e & 3));
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
 template <int HP>
 __device__ __forceinline__ void load_unit(const void* __restrict__ x, int64_t u, float v[8]) {
     if constexpr (HP == FP8Q_BF16) {
-        const uint4 w = reinterpret_cast<const uint4*>(x)[u];
+        const uint4 w = load_stream16(reinterpret_cast<const uint4*>(x) + u);
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -561,8 +563,12 @@ __device__ __forceinline__ void load_unit(const void* __restrict__ x, int64_t u,
             v[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
         }
     } else {
-        const float4 a = reinterpret_cast<const float4*>(x)[2 * u];
-        const float4 b = reinterpret_cast<const float4*>(x)[2 * u + 1];
+        const uint4 wa = load_stream16(reinterpret_cast<const uint4*>(x) + 2 * u);
+        const uint4 wb = load_stream16(reinterpret_cast<const uint4*>(x) + 2 * u + 1);
+        const float4 a = make_float4(__uint_as_float(wa.x), __uint_as_float(wa.y), __uint_as_float(wa.z),
+                                     __uint_as_float(wa.w));
+        const float4 b = make_float4(__uint_as_float(wb.x), __uint_as_float(wb.y), __uint_as_float(wb.z),
+                                     __uint_as_float(wb.w));
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }

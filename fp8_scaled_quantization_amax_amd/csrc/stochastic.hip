@@ -88,8 +88,9 @@ __global__ __launch_bounds__(256) void quantize_sr_kernel(const void* __restrict
                 v[2] = __uint_as_float(w.y << 16);
                 v[3] = __uint_as_float(w.y & 0xffff0000u);
             } else {
-                const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i0);
-                v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+                const uint4 w = load_stream16(reinterpret_cast<const float*>(x) + i0);
+                v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+                v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
             }
         } else {
 #pragma unroll

@@ -297,7 +297,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, int ntm, 
 //  * Epilogue: results are scaled (bf16: rounded by the hardware convert,
 //    round to nearest even, NaN stays NaN), staged through the LDS stage
 //    buffer the last step read, and stored as 16-byte row-contiguous pieces,
-//    so each store instruction writes whole cache lines.
+//    so each store instruction writes whole cache lines.  The stores carry
+//    the non-temporal hint: the output is not read again here, and keeping it
+//    out of the way leaves L2 to the operand panels (+2.7% measured; the same
+//    hint on the operand loads cost 16%, since those panels are shared by the
+//    tiles running on an XCD).
 
 // s_waitcnt lgkmcnt(n) (vmcnt, expcnt at their maxima) for an n that is a
 // compile-time constant after unrolling; n above 15 waits for 15, which is
@@ -647,7 +651,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
                     const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kEpPitch + ch * 16);
                     const int64_t m = m0 + wm + 32 * qq + row;
                     const int64_t n = n0 + wn + ch * 8;
-                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n) = d;
+                    if (m < M && n < N) __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n));
                 }
             }
         } else {
@@ -665,7 +669,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
                     const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kEpPitch32 + ch * 16);
                     const int64_t m = m0 + wm + 16 * i + row;
                     const int64_t n = n0 + wn + ch * 4;
-                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(g.C) + m * N + n) = d;
+                    if (m < M && n < N) __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(reinterpret_cast<float*>(g.C) + m * N + n));
                 }
             }
         }

@@ -24,7 +24,7 @@ namespace fp8q {
 // the workgroup tile is 256 x 128.  The rest follows the per-tensor kernel:
 // per-XCD tile ranges, direct-to-LDS operand loads one stage ahead (the last
 // K step of a tile loads the next tile's first stage), LDS-staged
-// row-contiguous stores.
+// row-contiguous stores with the non-temporal hint.
 //  * Row scales travel like the MX exponents: 16 bytes per row (four K
 //    blocks) per direct-to-LDS load, one group of four K steps ahead, double
 //    buffered; one 64-row load per wave per group instead of a scattered
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                     const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kPitch + ch * 16);
                     const int64_t m = m0 + wm + 32 * qq + row;
                     const int64_t n = n0 + wn + ch * 8;
-                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n) = d;
+                    if (m < M && n < N) __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + m * N + n));
                 }
             }
         } else {
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                     const u32x4 d = *reinterpret_cast<const u32x4*>(ep + row * kPitch + ch * 16);
                     const int64_t m = m0 + wm + 16 * i + row;
                     const int64_t n = n0 + wn + ch * 4;
-                    if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(g.C) + m * N + n) = d;
+                    if (m < M && n < N) __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(reinterpret_cast<float*>(g.C) + m * N + n));
                 }
             }
         }

@@ -272,7 +272,10 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(QuantArgs a, int64_
                                                              int vec_in, int vec_q, int vec_qt) {
     __shared__ uint32_t red[4];
     __shared__ __attribute__((aligned(16))) uint8_t lds_codes[kTile * kLdsStride];
-    __shared__ uint32_t lds_col[4 * 4 * kTile];   // cross-wave column maxima (axis-1 schemes)
+    // cross-wave column maxima (axis-1 schemes only; the others keep their LDS
+    // small so that more blocks fit on a CU)
+    constexpr bool kColumnTiles = SCHEME == kTileAxis1 || SCHEME == kMxAxis1;
+    __shared__ uint32_t lds_col[kColumnTiles ? 4 * 4 * kTile : 1];
 
     const int t = threadIdx.x;
     const int cc = t & 15, rg = t >> 4, wave = t >> 6;
@@ -302,14 +305,60 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(QuantArgs a, int64_
 
     uint32_t key_all = 0;   // running amax key (delayed scaling)
     const int64_t ntiles = ntr * ntc;
+    // A whole tile inside the matrix with aligned rows is loaded a tile ahead:
+    // its raw 16-byte pieces are in flight while the block works on the
+    // previous tile (edge tiles take the element-checked path on the spot).
+    constexpr int RAWN = HP == FP8Q_BF16 ? 1 : 2;   // 16-byte pieces per 8 elements
+    auto whole = [&](int64_t tl) {
+        return vec_in && (tl / ntc + 1) * kTile <= rows && (tl % ntc + 1) * kTile <= cols;
+    };
+    uint4 raw[8][RAWN];
+    auto raw_load = [&](int64_t tl) {
+        const int64_t rr = (tl / ntc) * kTile + rg, cl = (tl % ntc) * kTile + cc * 8;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const char* base = reinterpret_cast<const char*>(a.x) + ((rr + 16 * p) * cols + cl) * (HP == FP8Q_F32 ? 4 : 2);
+#pragma unroll
+            for (int q = 0; q < RAWN; ++q) raw[p][q] = load_stream16(base + 16 * q);
+        }
+    };
+    bool ahead = (int64_t)blockIdx.x < ntiles && whole(blockIdx.x);
+    if (ahead) raw_load(blockIdx.x);
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int64_t tr = tile / ntc, tc = tile % ntc;
         const int64_t r0 = tr * kTile, c0 = tc * kTile;
         const int64_t col = c0 + cc * 8;
 
         float v[8][8];
+        if (ahead) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) load8<HP>(a.x, rows, cols, r0 + rg + 16 * p, col, vec_in, v[p]);
+            for (int p = 0; p < 8; ++p) {
+                if constexpr (HP == FP8Q_BF16) {
+                    const uint32_t d[4] = {raw[p][0].x, raw[p][0].y, raw[p][0].z, raw[p][0].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[p][2 * j] = __uint_as_float(d[j] << 16);
+                        v[p][2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < RAWN; ++q) {
+                        v[p][4 * q] = __uint_as_float(raw[p][q].x);
+                        v[p][4 * q + 1] = __uint_as_float(raw[p][q].y);
+                        v[p][4 * q + 2] = __uint_as_float(raw[p][q].z);
+                        v[p][4 * q + 3] = __uint_as_float(raw[p][q].w);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 8; ++p) load8<HP>(a.x, rows, cols, r0 + rg + 16 * p, col, vec_in, v[p]);
+        }
+        {
+            const int64_t nt = tile + gridDim.x;
+            ahead = nt < ntiles && whole(nt);
+            if (ahead) raw_load(nt);
+        }
 
         uint32_t kp[8];   // per-row keys over this thread's 8 values
 #pragma unroll

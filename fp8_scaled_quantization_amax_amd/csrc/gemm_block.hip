@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "gemm_common.h"
 #include "launch.h"
@@ -21,10 +22,11 @@ namespace fp8q {
 // accumulator and its result is added into the fp32 accumulators with one
 // FMA per value: acc += (sA(m, kb) * sB(n, kb)) * partial.  Those FMAs need
 // the accumulators in VGPRs, so a wave owns 128 x 64 outputs (128 VGPRs) and
-// the workgroup tile is 256 x 128.  The rest follows the per-tensor kernel:
-// per-XCD tile ranges, direct-to-LDS operand loads one stage ahead (the last
-// K step of a tile loads the next tile's first stage), LDS-staged
-// row-contiguous stores with the non-temporal hint.
+// the workgroup tile is 256 x 128.  Like the per-tensor kernel it walks
+// per-XCD tile ranges with direct-to-LDS operand loads and LDS-staged
+// row-contiguous stores with the non-temporal hint.  Its K steps are half as
+// long (32 MFMAs per wave), so it keeps three 48 KB stages and loads two steps
+// ahead; the last two K steps of a tile load the next tile's first two stages.
 //  * Row scales travel like the MX exponents: 16 bytes per row (four K
 //    blocks) per direct-to-LDS load, one group of four K steps ahead, double
 //    buffered; one 64-row load per wave per group instead of a scattered
@@ -33,8 +35,13 @@ namespace fp8q {
 //  * With block-scaled B the 64 columns of a wave share one scale per K
 //    block (one uniform load per step, a step ahead), so the FMA factor is
 //    one product per fragment row and step.
-//  * The FMAs of fragment row i run under the MFMAs of row i + 1; those of
-//    the last row wait until after the next barrier.
+//  * The FMAs of fragment row i run under the MFMAs of row i + 1.  The last
+//    row's MFMAs (and the FMAs of the last two rows) run after the next
+//    barrier, from registers, while the next step's fragments are read.
+//  * What bounds it: per 1024 MFMA cycles of a K step a CU moves 96 KB of
+//    fragment reads and 48 KB of operand writes through LDS, and every
+//    MFMA is followed by four FMAs.  A 128 x 128 wave tile would halve the
+//    LDS traffic per MFMA but needs 256 accumulator VGPRs, all there are.
 // bytes spanned by a fp32 scale array (rows >> rshift, ld, kstride) over nkb K blocks
 __device__ __forceinline__ int64_t scale_bytes(const GemmScale& s, int64_t rows, int64_t nkb) {
     return ((((rows - 1) >> s.rshift) * s.ld + (nkb - 1) * s.kstride) + 1) * 4;
@@ -49,8 +56,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
     constexpr int BNb = 128;
     constexpr int kStage = kTileBytes + BNb * BK;   // A 256 x 128 + B 128 x 128 bytes
     constexpr int kScA = BM * 16, kScGroup = kScA + (BROW ? BNb * 16 : 0);
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[2 * kStage + 2 * kScGroup];
-    uint8_t* const lds_sc = lds_all + 2 * kStage;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[3 * kStage + 2 * kScGroup];
+    uint8_t* const lds_sc = lds_all + 3 * kStage;
     const int64_t M = g.M, N = g.N, K = g.K;
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
     const int wm = (w >> 1) * 128, wn = (w & 1) * 64;
@@ -113,130 +120,158 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
     float sbn = 0.f;   // block-scaled B: the wave's scale of the next K step
 
     TileState cur = tile_state(logical);
+    // stage 0, the first scale group (and B block scale), then stage 1: the
+    // wait at the top of a step leaves only the 12 loads of the following
+    // stage in flight
 #pragma unroll
     for (int u = 0; u < 12; ++u) stage_load(cur, 0u, lds_all, u);
     group_load(cur, 0, 0);
     if constexpr (!BROW) sbn = load_f32(rsb, cur.sb_row);
+#pragma unroll
+    for (int u = 0; u < 12; ++u) stage_load(cur, (uint32_t)BK, lds_all + kStage, u);
 
     constexpr int NSB = BROW ? 16 : 1;
     v4f acc[8][4];
-    int par = 0, gpar = 0;
+    // p: the MFMA partials of fragment rows of parity 0 / 1
+    v4f p[2][4];
+    v8i b[4], a[2];
+    // FMA factors: sf[i] for fragment row i, the A row scale times the B
+    // block scale (or the A row scale alone, times the B row scales sbr per
+    // value); sraw / sbc: the step's scales as read
+    float sf[8], sbr[NSB], sraw[8];
+    int par = 0, gpar = 0;   // buffers (of 3 / of 2) holding the tile's stage 0 / first scale group
     while (true) {
         const int next = logical + per;
         const bool has_next = next < hi;
-        // without a next tile the last step re-loads this tile's first stage
-        // into the free buffer: harmless, and it keeps the step branch-free
+        // without a next tile the last two steps re-load this tile's first
+        // stages into free buffers: harmless, and it keeps the steps branch-free
         const TileState nxt = tile_state(has_next ? next : logical);
-        // p: the MFMA partials of fragment rows of parity 0 / 1.  Row 7's
-        // are added after the next barrier, under the next step's first
-        // fragment reads; before the first step they are zero.
-        v4f p[2][4];
-        float sf7 = 0.f, sb7[NSB];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[1][j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < NSB; ++q) sb7[q] = 0.f;
-        auto row_fma = [&](int i, float s, const float* sb) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[i][j][r] = __builtin_fmaf(p[i & 1][j][r], BROW ? s * sb[4 * j + r] : s, acc[i][j][r]);
+        auto mfma_one = [&](int i, int j) {
+            p[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                b[j], a[i & 1], v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA, 0, 0, 0, 0);
         };
-        for (int kt = 0; kt < nk; ++kt) {
-            // this stage and its scales landed; every wave is done with the other buffers
-            vm_wait<0>();
+        auto fma_one = [&](int i, int j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[i][j][r] = __builtin_fmaf(p[i & 1][j][r], BROW ? sf[i] * sbr[4 * j + r] : sf[i], acc[i][j][r]);
+        };
+        // One K step.  Stage kt sits in buffer (par + kt) % 3; the step loads
+        // stage kt + 2 (of this tile, or the next tile's stage kt + 2 - nk)
+        // into the buffer every wave finished with before the barrier.  With
+        // DEF the previous step's fragment row 7 is still open: its MFMAs run
+        // first, straight after the barrier and from registers only, while
+        // this step's fragments are read; its FMAs follow under row 0's MFMAs.
+        // Row i's FMAs run under row i + 1's MFMAs, whose partial they do not
+        // touch; row i + 1's A fragment is read into the registers row i - 1
+        // used.  The scheduling barriers keep this order (left free, the
+        // compiler put each FMA group right behind the MFMA producing it).
+        auto step = [&](auto def_c, int kt) {
+            constexpr bool DEF = decltype(def_c)::value;
+            // this stage, its scales and the B block scale landed; every wave
+            // is done with the buffer the loads below overwrite
+            vm_wait<12>();
             stage_barrier();
-            const bool last = kt + 1 == nk;
+            const bool last = kt + 1 == nk, next2 = kt + 2 >= nk;
             const int gi = kt >> 2;
             // scale groups: the next one of this tile at a group's first step,
             // the next tile's first one at the last step
             if (last) group_load(nxt, (ngroups + gpar) & 1, 0);
             else if ((kt & 3) == 0 && gi + 1 < ngroups) group_load(cur, (gi + 1 + gpar) & 1, gi + 1);
-            TileState ld;   // field by field: a selected reference would live in scratch memory
-            ld.a.e = last ? nxt.a.e : cur.a.e;
-            ld.a.o = last ? nxt.a.o : cur.a.o;
-            ld.b.e = last ? nxt.b.e : cur.b.e;
-            ld.b.o = last ? nxt.b.o : cur.b.o;
-            ld.sa_row = last ? nxt.sa_row : cur.sa_row;
-            ld.sb_row = last ? nxt.sb_row : cur.sb_row;
-            const uint32_t ko = last ? 0u : (uint32_t)(kt + 1) * BK;
-            const uint8_t* la = lds_all + ((kt + par) & 1) * kStage;
-            const uint8_t* lb = la + kTileBytes;
-            uint8_t* dst = lds_all + ((kt + 1 + par) & 1) * kStage;
-            v8i b[4], a[2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = frag2(lb, wn + 16 * j);
-            a[0] = frag2(la, wm);
-            a[1] = frag2(la, wm + 16);
-#pragma unroll
-            for (int u = 0; u < 12; ++u) stage_load(ld, ko, dst, u);
             float sbc = 0.f;
             if constexpr (!BROW) {
                 sbc = sbn;
-                sbn = load_f32(rsb, ld.sb_row + (last ? 0u : (uint32_t)(kt + 1) * ksb4));
+                sbn = load_f32(rsb, last ? nxt.sb_row : cur.sb_row + (uint32_t)(kt + 1) * ksb4);
             }
-            // this step's scales: A rows of the lane's 8 fragment rows; B rows
-            // of its 4 x 4 columns (row scales) or the wave's block scale
+            TileState ld;   // field by field: a selected reference would live in scratch memory
+            ld.a.e = next2 ? nxt.a.e : cur.a.e;
+            ld.a.o = next2 ? nxt.a.o : cur.a.o;
+            ld.b.e = next2 ? nxt.b.e : cur.b.e;
+            ld.b.o = next2 ? nxt.b.o : cur.b.o;
+            const uint32_t ko = (uint32_t)(next2 ? kt + 2 - nk : kt + 2) * BK;
+            const uint8_t* la = lds_all + ((par + kt) % 3) * kStage;
+            const uint8_t* lb = la + kTileBytes;
+            uint8_t* dst = lds_all + ((par + kt + 2) % 3) * kStage;
             const uint8_t* gs = lds_sc + ((gi + gpar) & 1) * kScGroup + 4 * (kt & 3);
-            float sf[8], sbr[NSB];
+            __builtin_amdgcn_sched_barrier(0);
+            a[0] = frag2(la, wm);
+            if constexpr (DEF) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float sa = *reinterpret_cast<const float*>(gs + (wm + 16 * i + (l & 15)) * 16);
-                sf[i] = BROW ? sa : sa * sbc;
+                for (int j = 0; j < 4; ++j) {
+                    mfma_one(7, j);
+                    b[j] = frag2(lb, wn + 16 * j);
+#pragma unroll
+                    for (int u = 3 * j; u < 3 * j + 3; ++u) stage_load(ld, ko, dst, u);
+                    fma_one(6, j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = frag2(lb, wn + 16 * j);
+#pragma unroll
+                for (int u = 0; u < 12; ++u) stage_load(ld, ko, dst, u);
             }
+            a[1] = frag2(la, wm + 16);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mfma_one(0, j);
+                if constexpr (DEF) fma_one(7, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // this step's scales, after the last use of the previous step's;
+            // row i's factor is formed where its FMAs start, so that no
+            // instruction waits for these reads before it must
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                sraw[i] = *reinterpret_cast<const float*>(gs + (wm + 16 * i + (l & 15)) * 16);
             if constexpr (BROW) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
                     sbr[q] = *reinterpret_cast<const float*>(gs + kScA + (wn + 16 * (q >> 2) + 4 * (l >> 4) + (q & 3)) * 16);
             }
-            row_fma(7, sf7, sb7);
-            // Fragment row i + 1's MFMAs run while row i's partials are added:
-            // MFMA (i + 1, j), then the four FMAs of (i, j), whose partial was
-            // produced four MFMAs earlier.  Row i + 2's fragment is read into
-            // the registers row i used.  The scheduling barriers keep this
-            // order (left free, the compiler put each FMA group right behind
-            // the MFMA producing it and waited for that MFMA with s_nops).
-            auto mfma_one = [&](int i, int j) {
-                p[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    b[j], a[i & 1], v4f{0.f, 0.f, 0.f, 0.f}, kFmtB, kFmtA, 0, 0, 0, 0);
-            };
-            auto fma_one = [&](int i, int j, float sv, const float* sb) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[i][j][r] = __builtin_fmaf(p[i & 1][j][r], BROW ? sv * sb[4 * j + r] : sv, acc[i][j][r]);
-            };
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mfma_one(0, j);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < 7; ++i) {
+            for (int i = 1; i < 7; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    mfma_one(i + 1, j);
-                    if (j == 0 && i + 2 < 8) a[i & 1] = frag2(la, wm + 16 * (i + 2));
-                    fma_one(i, j, sf[i], sbr);
+                    mfma_one(i, j);
+                    if (j == 0) {
+                        a[(i + 1) & 1] = frag2(la, wm + 16 * (i + 1));
+                        sf[i - 1] = BROW ? sraw[i - 1] : sraw[i - 1] * sbc;
+                    }
+                    fma_one(i - 1, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            sf7 = sf[7];
 #pragma unroll
-            for (int q = 0; q < NSB; ++q) sb7[q] = sbr[q];
+            for (int i = 6; i < 8; ++i) sf[i] = BROW ? sraw[i] : sraw[i] * sbc;
+            // every read of this stage has returned before the barrier that
+            // frees its buffer
             lds_wait_all();
+        };
+        using T = std::true_type;
+        using F = std::false_type;
+        step(F{}, 0);
+        for (int kt = 1; kt < nk; ++kt) step(T{}, kt);
+        // the last step's row 7
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mfma_one(7, j);
+            fma_one(6, j);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        row_fma(7, sf7, sb7);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fma_one(7, j);
         // every wave is done reading the last stage before it is reused
         stage_barrier();
-
         int tm, tn;
         tile_coords(logical, ntm, ntn, tm, tn);
         const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNb;
-        uint8_t* ep0 = lds_all + ((nk - 1 + par) & 1) * kStage;
+        uint8_t* ep0 = lds_all + ((par + nk - 1) % 3) * kStage;
         if constexpr (OUT == FP8Q_BF16) {
             typedef float v2f_t __attribute__((ext_vector_type(2)));
             typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
@@ -286,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
         }
         if (!has_next) break;
         logical = next;
-        par = (nk + par) & 1;
+        par = (par + nk) % 3;
         gpar = (ngroups + gpar) & 1;
         cur = nxt;
     }

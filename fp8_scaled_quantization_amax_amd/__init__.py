@@ -72,6 +72,7 @@ def lib():
             "fp8_gemm_scaled_NT": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
             "fp8_gemm_scaled_NN": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
             "fp8_gemm_scaled_TN": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
+            "fp8q_mfma_loop": (I, [I, I, P, P]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -147,6 +148,15 @@ class DelayedState:
 
 
 # ---------------------------------------------------------------- amax / quantize
+def fp8q_mfma_loop(blocks, iters, device="cuda"):
+    """Measurement aid (not the FP8 path): `blocks` x 256 threads, each wave
+    running `iters` rounds of 8 register-only FP8 MFMAs; returns the per-thread
+    outputs (each exactly 4096 * iters for iters <= 4096)."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    _check(lib().fp8q_mfma_loop(blocks, iters, _ptr(out), _stream()))
+    return out
+
+
 def fp8_amax(x, ws=None):
     """amax = max|x| over all elements (float32 tensor [1])."""
     hp = _hp(x)

@@ -445,6 +445,17 @@ int fp8_quantize_per_tensor_rht(const void* x, int hp, int64_t rows, int64_t col
     return ok();
 }
 
+int fp8q_mfma_loop(int blocks, int iters, float* out, void* stream) {
+    if (blocks <= 0 || iters <= 0 || out == nullptr)
+        return fail(FP8Q_EINVAL, "blocks and iters must be positive and out non-NULL");
+    int r;
+    if ((r = check_device()) != FP8Q_OK) return r;
+    if ((r = launched(fp8q::launch_mfma_loop(blocks, iters, out, reinterpret_cast<hipStream_t>(stream)),
+                      "mfma loop")) != FP8Q_OK)
+        return r;
+    return ok();
+}
+
 int fp8_quantize_tile1x128(const void* x, int hp, int64_t rows, int64_t cols, int axis, int fmt, uint8_t* q,
                            uint8_t* qT, float* scales, unsigned flags, void* stream) {
     int r;

@@ -85,6 +85,10 @@ hipError_t launch_quantize_rht(const void* x, int hp, int64_t rows, int64_t cols
                                float* partials, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
                                hipStream_t s);
 
+// Measurement aid: `blocks` workgroups of 256 threads, each wave running
+// `iters` rounds of 8 register-only FP8 MFMAs; out holds blocks * 256 floats.
+hipError_t launch_mfma_loop(int blocks, int iters, float* out, hipStream_t s);
+
 // Rowwise quantization: one fp32 scale per row (axis 0) or per column (axis
 // 1) into scales, codes into q [rows, cols], and (if qT != NULL) their
 // transpose into qT [cols, rows].  Axis 1 keeps integer maxima in `scales`

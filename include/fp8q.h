@@ -345,6 +345,18 @@ int fp8_gemm_scaled_TN(int64_t M, int64_t N, int64_t K, const fp8q_operand* A,
                        const fp8q_operand* B, void* C, int c_dtype,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ measurement aid
+ * fp8q_mfma_loop: not part of the FP8 path.  Launches `blocks` workgroups of
+ * 256 threads; every wave runs `iters` rounds of 8 independent 16x16x128
+ * E4M3 MFMAs on operands held in registers (all codes 1.0) and writes one
+ * float per thread to out (device, blocks * 256 floats, caller-owned): exactly
+ * 4096 * iters, exact for iters <= 4096.  Each round of a wave is 8 * 2 * 16 * 16 * 128
+ * FLOP, so timing the call gives the sustained FP8 MFMA rate with no memory
+ * traffic: the measured ceiling beside the nominal dense peak.
+ * EINVAL for blocks <= 0, iters <= 0 or out == NULL; enqueued on `stream`.
+ */
+int fp8q_mfma_loop(int blocks, int iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,8 @@ def lib():
         U32, U64 = ctypes.c_uint32, ctypes.c_uint64
         L.orc_philox4x32_10.restype, L.orc_philox4x32_10.argtypes = None, [P, P, P]
         L.orc_sr_word.restype, L.orc_sr_word.argtypes = U32, [U64, U64, U64]
+        L.orc_set_threads.restype, L.orc_set_threads.argtypes = None, [I32]
+        L.orc_max_threads.restype, L.orc_max_threads.argtypes = I32, []
         L.orc_encode_sr.restype, L.orc_encode_sr.argtypes = ctypes.c_uint8, [F, U32, I32, I32]
         L.orc_quantize_per_tensor_sr.restype = None
         L.orc_quantize_per_tensor_sr.argtypes = [P, I32, I64, I32, I32, U64, U64, P, P, P]
@@ -116,6 +118,16 @@ def encode_compare_range(lo, hi, fmt, ref):
     first = ctypes.c_uint64(0)
     bad = lib().orc_encode_compare_range(lo, hi, fmt, _ptr(ref), ctypes.byref(first))
     return bad, first.value
+
+
+# ---------------------------------------------------------------- threads (timing only)
+def set_threads(n):
+    """Thread count of the oracle's parallel loops (results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads():
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------- amax / scale / cast

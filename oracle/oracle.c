@@ -36,6 +36,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_E4M3 0
 #define ORC_E5M2 1
@@ -580,4 +583,23 @@ int64_t orc_encode_compare_range(uint64_t lo, uint64_t hi, int fmt, const uint8_
     }
     if (first_bad) *first_bad = first;
     return bad;
+}
+
+/* Thread count of the parallel loops, for timing the oracle on one core or on
+ * all of them.  Results do not depend on it: the maxima are order-free and
+ * the GEMM sums integers exactly. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

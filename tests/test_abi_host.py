@@ -148,6 +148,14 @@ def test_gemm_workspace_sizes():
     assert L.fp8_gemm_workspace_bytes(0, 100, 256, 256, R(A), R(B)) == ctypes.c_size_t(-1).value
 
 
+def test_mfma_loop_validation():
+    L = fq.lib()
+    fake = ctypes.c_void_p(0x10000)
+    assert L.fp8q_mfma_loop(0, 16, fake, None) == fq.EINVAL
+    assert L.fp8q_mfma_loop(4, 0, fake, None) == fq.EINVAL
+    assert L.fp8q_mfma_loop(4, 16, None, None) == fq.EINVAL
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fq, "_lib", None)
     monkeypatch.setattr(fq, "LIB_PATH", str(tmp_path / "missing.so"))

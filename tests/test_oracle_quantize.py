@@ -239,3 +239,19 @@ def test_tile_roundtrip_bound_per_tile(orc):
         y = orc.decode_array(q, fmt) * s
         normal = np.abs(x / s) >= sn
         assert (np.abs(y - x) / np.abs(x))[normal].max() <= bound
+
+
+def test_results_do_not_depend_on_thread_count(orc):
+    """The oracle is timed on one core and on all of them: its codes, scale
+    and amax must be the same either way (order-free maxima)."""
+    x = workloads.normal((257, 384), 3.0, 77, torch.bfloat16)
+    bits = workloads.bf16_bits(x)
+    n = orc.max_threads()
+    try:
+        orc.set_threads(1)
+        q1, s1, a1 = orc.quantize_per_tensor(bits, E4M3)
+        orc.set_threads(max(n, 2))
+        qn, sn, an = orc.quantize_per_tensor(bits, E4M3)
+    finally:
+        orc.set_threads(n)
+    assert np.array_equal(q1, qn) and s1 == sn and a1 == an

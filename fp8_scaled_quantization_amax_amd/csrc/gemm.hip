@@ -457,9 +457,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
     // u (0..15) of a wave: MODE 1 = stage kt+1 of this tile, MODE 2 = stage 0
     // of the next tile; both go to the buffer the current step does not read.
     int par = 0;
+    // K direction of the current tile (non-MX modes): consecutive tiles of a
+    // workgroup walk K forward and backward in turn.  The tiles an XCD runs
+    // at the same time move on together to tiles over the same A panels, so
+    // a tile that starts where the previous ones ended finds those K blocks
+    // of the panels still in L2.  (MX keeps the forward walk: its scale
+    // groups follow K.)
+    int rev = 0;
+    auto kblock = [&](int r, int kt) { return (uint32_t)(r ? nk - 1 - kt : kt) * BK; };
     auto dma = [&](auto mode_c, int kt, int u) {
         constexpr int MODE = decltype(mode_c)::value;
-        const uint32_t ko = MODE == 1 ? (uint32_t)(kt + 1) * BK : 0u;
+        const uint32_t ko = MODE == 1 ? kblock(rev, kt + 1) : kblock(MX ? 0 : rev ^ 1, 0);
         uint8_t* dst = lds_ab[(kt + 1 + par) & 1];
         if (u < 8) {
             tile_load(ra, MODE == 1 ? da : na, ko, dst, u);
@@ -676,6 +684,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
         if (!has_next) break;
         logical = next;
         par = (nk + par) & 1;
+        if constexpr (!MX) rev ^= 1;
         gpar = (ngroups + gpar) & 1;
         tm = ntm_;
         tn = ntn_;

@@ -16,6 +16,7 @@ F32, BF16 = 0, 1
 PER_TENSOR, TILE_1x128, BLOCK_128x128, MX32, ROWWISE = 0, 1, 2, 3, 4
 CURRENT, DELAYED = 0, 1
 SATURATE = 1
+COUNT_OVERFLOW = 2
 HISTORY_LEN = 16
 
 OK, EINVAL, EALIGN, EUNSUPPORTED, EDEVICE, ELAUNCH, EWORKSPACE = range(7)
@@ -143,6 +144,12 @@ class DelayedState:
         return self.buf[64:68].view(torch.int32)
 
     @property
+    def overflows(self):
+        """Overflowing elements of the last delayed call made with
+        count_overflow (0 after a call without it)."""
+        return self.buf[68:72].view(torch.int32)
+
+    @property
     def last_scale(self):
         return self.buf[76:80].view(torch.float32)
 
@@ -166,8 +173,10 @@ def fp8_amax(x, ws=None):
     return out
 
 
-def fp8_quantize_per_tensor(x, fmt=E4M3, scaling=CURRENT, state=None, emit_t=False, saturate=False, ws=None):
-    """Per-tensor quantization of a 2-D (or 1-D) tensor; returns (q, qT, scale, amax)."""
+def fp8_quantize_per_tensor(x, fmt=E4M3, scaling=CURRENT, state=None, emit_t=False, saturate=False, ws=None,
+                            count_overflow=False):
+    """Per-tensor quantization of a 2-D (or 1-D) tensor; returns (q, qT, scale, amax).
+    count_overflow (delayed scaling): the overflowing elements go to state.overflows."""
     hp = _hp(x)
     rows, cols = _rows_cols(x)
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
@@ -177,8 +186,9 @@ def fp8_quantize_per_tensor(x, fmt=E4M3, scaling=CURRENT, state=None, emit_t=Fal
     ws = reduce_workspace(x.device) if ws is None else ws
     st = state.ptr() if state is not None else None
     _check(lib().fp8_quantize_per_tensor(_ptr(x), hp, rows, cols, fmt, scaling, st, _ptr(q), _ptr(qT),
-                                         _ptr(scale), _ptr(amax), SATURATE if saturate else 0, _ptr(ws),
-                                         ws.numel(), _stream()))
+                                         _ptr(scale), _ptr(amax),
+                                         (SATURATE if saturate else 0) | (COUNT_OVERFLOW if count_overflow else 0),
+                                         _ptr(ws), ws.numel(), _stream()))
     return q, qT, scale, amax
 
 
@@ -285,10 +295,11 @@ class GemmOperand:
 
     @staticmethod
     def autocast(x, fmt, granularity=PER_TENSOR, scaling=CURRENT, state=None, scale_out=None, amax_out=None,
-                 saturate=False):
+                 saturate=False, count_overflow=False):
         hp = _hp(x)
+        flags = (SATURATE if saturate else 0) | (COUNT_OVERFLOW if count_overflow else 0)
         op = Operand(data=x.data_ptr(), quantized=0, format=fmt, granularity=granularity, hp=hp, scaling=scaling,
-                     flags=SATURATE if saturate else 0, state=None if state is None else state.buf.data_ptr(),
+                     flags=flags, state=None if state is None else state.buf.data_ptr(),
                      scale_out=None if scale_out is None else scale_out.data_ptr(),
                      amax_out=None if amax_out is None else amax_out.data_ptr())
         return GemmOperand(op, (x, state, scale_out, amax_out))

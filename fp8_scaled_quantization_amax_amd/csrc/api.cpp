@@ -73,7 +73,7 @@ int launched(hipError_t e, const char* what) {
 
 bool valid_hp(int hp) { return hp == FP8Q_F32 || hp == FP8Q_BF16; }
 bool valid_fmt(int f) { return f == FP8Q_E4M3 || f == FP8Q_E5M2; }
-bool valid_flags(unsigned f) { return (f & ~FP8Q_SATURATE) == 0; }
+bool valid_flags(unsigned f) { return (f & ~(FP8Q_SATURATE | FP8Q_COUNT_OVERFLOW)) == 0; }
 size_t hp_size(int hp) { return hp == FP8Q_BF16 ? 2 : 4; }
 
 constexpr size_t kAlign = 256;
@@ -126,6 +126,8 @@ int validate_operand(const fp8q_operand* o, const char* name, int64_t K) {
                 return fail(FP8Q_EUNSUPPORTED, "operand %s: delayed scaling is per-tensor only", name);
             if (o->state == nullptr) return fail(FP8Q_EINVAL, "operand %s: delayed scaling needs a state", name);
         }
+        if ((o->flags & FP8Q_COUNT_OVERFLOW) && !(o->scaling == FP8Q_DELAYED && gr == FP8Q_PER_TENSOR))
+            return fail(FP8Q_EINVAL, "operand %s: FP8Q_COUNT_OVERFLOW needs delayed per-tensor scaling", name);
     }
     return FP8Q_OK;
 }
@@ -229,6 +231,7 @@ int autocast_operand(const fp8q_operand* o, bool kcontig, int64_t R, int64_t K, 
             const bool delayed = o->scaling == FP8Q_DELAYED;
             a.scheme = delayed ? fp8q::kPerTensorDelayed : fp8q::kPerTensorCurrent;
             a.state = o->state;
+            a.count_overflow = delayed && (o->flags & FP8Q_COUNT_OVERFLOW) != 0;
             a.scale_out = o->scale_out != nullptr ? o->scale_out : reinterpret_cast<float*>(ws_scale);
             *scale_used = a.scale_out;
             a.amax_out = o->amax_out;
@@ -355,13 +358,16 @@ int fp8_amax(const void* x, int hp, int64_t n, float* amax_out, void* ws, size_t
     return ok();
 }
 
+// allowed: the flags this entry point takes (FP8Q_COUNT_OVERFLOW only where
+// delayed scaling keeps the count)
 static int check_quant_common(const void* x, int hp, int64_t rows, int64_t cols, int fmt, const uint8_t* q,
-                              unsigned flags) {
+                              unsigned flags, unsigned allowed = FP8Q_SATURATE) {
     if (x == nullptr || q == nullptr) return fail(FP8Q_EINVAL, "x and q are required");
     if (rows <= 0 || cols <= 0) return fail(FP8Q_EINVAL, "rows and cols must be positive");
     if (!valid_hp(hp)) return fail(FP8Q_EINVAL, "unknown element type %d", hp);
     if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "unknown format %d", fmt);
     if (!valid_flags(flags)) return fail(FP8Q_EINVAL, "unknown flags %#x", flags);
+    if (flags & ~allowed) return fail(FP8Q_EINVAL, "flags %#x not taken by this call", flags & ~allowed);
     if ((uintptr_t)x % hp_size(hp) != 0) return fail(FP8Q_EALIGN, "x is not aligned to its element type");
     return FP8Q_OK;
 }
@@ -370,10 +376,12 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, i
                             fp8q_delayed_state* state, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
                             unsigned flags, void* ws, size_t ws_bytes, void* stream) {
     int r;
-    if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags)) != FP8Q_OK) return r;
+    if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags, FP8Q_SATURATE | FP8Q_COUNT_OVERFLOW)) != FP8Q_OK) return r;
     if (scale_out == nullptr) return fail(FP8Q_EINVAL, "scale_out is required");
     if (scaling != FP8Q_CURRENT && scaling != FP8Q_DELAYED) return fail(FP8Q_EINVAL, "unknown scaling %d", scaling);
     if (scaling == FP8Q_DELAYED && state == nullptr) return fail(FP8Q_EINVAL, "delayed scaling needs a state");
+    if ((flags & FP8Q_COUNT_OVERFLOW) && scaling != FP8Q_DELAYED)
+        return fail(FP8Q_EINVAL, "FP8Q_COUNT_OVERFLOW needs delayed scaling (the count lives in its state)");
     if (ws == nullptr || ws_bytes < fp8q::kReduceWsBytes)
         return fail(FP8Q_EWORKSPACE, "reduce workspace of %zu bytes needed", fp8q::kReduceWsBytes);
     if ((r = check_device()) != FP8Q_OK) return r;
@@ -391,6 +399,7 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, i
     a.scale_out = scale_out;
     a.amax_out = amax_out;
     a.scheme = scaling == FP8Q_DELAYED ? fp8q::kPerTensorDelayed : fp8q::kPerTensorCurrent;
+    a.count_overflow = (flags & FP8Q_COUNT_OVERFLOW) != 0;
     if ((r = launched(fp8q::launch_amax_partials(x, hp, rows * cols, partials, a.nparts,
                                                  scaling == FP8Q_DELAYED ? state : nullptr, s),
                       "amax")) != FP8Q_OK)

@@ -54,15 +54,18 @@ struct QuantArgs {
     fp8q_delayed_state* state;
     float* scale_out;
     float* amax_out;
+    bool count_overflow;   // delayed scaling: add overflowing elements to state->overflows
 };
 
 // amax partial maxima over n elements: one float per block into partials[0..nparts).
-// If gate != NULL the grid does nothing unless gate's history is all zero.
+// If gate != NULL the grid does nothing unless gate's history is all zero; in
+// either case it first clears gate->overflows (the delayed cast that follows
+// counts into it).
 // If keys != NULL the blocks instead fold their maxima among themselves (keys and
 // ticket counters of the reduce workspace) and the last block writes *amax_out.
 int amax_partials_grid(int64_t n);
 hipError_t launch_amax_partials(const void* x, int hp, int64_t n, float* partials, int nparts,
-                                const fp8q_delayed_state* gate, hipStream_t s, uint32_t* keys = nullptr,
+                                fp8q_delayed_state* gate, hipStream_t s, uint32_t* keys = nullptr,
                                 uint32_t* ctrs = nullptr, float* amax_out = nullptr);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);

@@ -78,12 +78,14 @@ __device__ __forceinline__ uint32_t fold_keys_256(const uint32_t* keys, int n, u
 template <int HP>
 __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restrict__ x, int64_t n,
                                                             float* __restrict__ partials,
-                                                            const fp8q_delayed_state* __restrict__ gate,
+                                                            fp8q_delayed_state* __restrict__ gate,
                                                             int vec, uint32_t* keys, uint32_t* ctrs,
                                                             float* amax_out) {
     __shared__ uint32_t red[4];
     __shared__ uint32_t last;
     if (gate != nullptr) {
+        // the delayed cast launched next counts its overflows into the state
+        if (blockIdx.x == 0 && threadIdx.x == 0) gate->overflows = 0u;
         uint32_t h = 0;
 #pragma unroll
         for (int i = 0; i < FP8Q_HISTORY_LEN; ++i) h |= __float_as_uint(gate->amax_history[i]);
@@ -164,7 +166,7 @@ int amax_partials_grid(int64_t n) {
 }
 
 hipError_t launch_amax_partials(const void* x, int hp, int64_t n, float* partials, int nparts,
-                                const fp8q_delayed_state* gate, hipStream_t s, uint32_t* keys,
+                                fp8q_delayed_state* gate, hipStream_t s, uint32_t* keys,
                                 uint32_t* ctrs, float* amax_out) {
     const int vec = ((uintptr_t)x % 16) == 0;
     if (hp == FP8Q_BF16)
@@ -227,6 +229,29 @@ __device__ __forceinline__ void store_tile_transposed(const uint8_t* lds, uint8_
             for (int i = 0; i < 16 && rbase + i < rows; ++i) dst[i] = (uint8_t)(col[j][i >> 2] >> (8 * (i & 3)));
         }
     }
+}
+
+// ------------------------------------------------------------------ overflow count
+
+// 1 if the cast of a finite x, with quotient v = RN32(x / s), overflows the
+// format: the non-saturating conversion gives NaN (E4M3: |v| > 464; 464
+// itself is the tie that rounds to the even-mantissa 448) or +-Inf (E5M2:
+// |v| >= 61440, the tie above 57344 that rounds to even 2^16).
+template <int FMT>
+__device__ __forceinline__ uint32_t overflowed(float x, float v) {
+    const bool finite = (__float_as_uint(x) & 0x7fffffffu) < 0x7f800000u;
+    const float av = __builtin_fabsf(v);
+    return finite && (FMT == FP8Q_E4M3 ? av > 464.0f : av >= 61440.0f) ? 1u : 0u;
+}
+
+// Adds the block's overflow count to the delayed state (integer atomics:
+// the total does not depend on their order).
+__device__ __forceinline__ void add_overflows(fp8q_delayed_state* st, uint32_t n, uint32_t* lds_sum) {
+    if (threadIdx.x == 0) *lds_sum = 0u;
+    __syncthreads();
+    if (n != 0u) atomicAdd(lds_sum, n);
+    __syncthreads();
+    if (threadIdx.x == 0 && *lds_sum != 0u) atomicAdd(&st->overflows, *lds_sum);
 }
 
 // ------------------------------------------------------------------ tiled quantize
@@ -304,6 +329,7 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(QuantArgs a, int64_
     if constexpr (kPerTensor) r_pt = 1.0f / s_pt;
 
     uint32_t key_all = 0;   // running amax key (delayed scaling)
+    uint32_t nov = 0;       // overflowing elements (delayed scaling, COUNT_OVERFLOW)
     const int64_t ntiles = ntr * ntc;
     // A whole tile inside the matrix with aligned rows is loaded a tile ahead:
     // its raw 16-byte pieces are in flight while the block works on the
@@ -377,9 +403,17 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(QuantArgs a, int64_
             }
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
-                float q[8];
+                float d[8], q[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(div_by_scale(v[p][e], s_pt, r_pt));
+                for (int e = 0; e < 8; ++e) {
+                    d[e] = div_by_scale(v[p][e], s_pt, r_pt);
+                    q[e] = saturate<FMT, SAT>(d[e]);
+                }
+                // elements outside the matrix were loaded as zeros: never counted
+                if (SCHEME == kPerTensorDelayed && a.count_overflow) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) nov += overflowed<FMT>(v[p][e], d[e]);
+                }
                 codes[p][0] = pack4<FMT>(q[0], q[1], q[2], q[3]);
                 codes[p][1] = pack4<FMT>(q[4], q[5], q[6], q[7]);
             }
@@ -538,7 +572,8 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(QuantArgs a, int64_
         // The grid's amax goes into the history after every block has cast with
         // the old scale: the last block to finish folds the per-block maxima
         // and records it.
-        __shared__ uint32_t last;
+        __shared__ uint32_t last, ov_sum;
+        if (a.count_overflow) add_overflows(a.state, nov, &ov_sum);
         const uint32_t k = block_max_u32_256(key_all, red);
         if (t == 0) last = grid_done(a.keys, a.ctrs, k);
         __syncthreads();
@@ -653,6 +688,7 @@ __global__ __launch_bounds__(256) void quantize_flat_kernel(QuantArgs a, int64_t
     const int64_t b0 = (int64_t)blockIdx.x * per;
     const int64_t b1 = b0 + per < nunits ? b0 + per : nunits;
     uint32_t key_all = 0;
+    uint32_t nov = 0;   // overflowing elements (delayed scaling, COUNT_OVERFLOW)
     for (int64_t base = b0; base < b1; base += 256 * UNR) {
         float v[UNR][8];
         // units past the run's end re-read its last unit (loads stay
@@ -672,8 +708,16 @@ __global__ __launch_bounds__(256) void quantize_flat_kernel(QuantArgs a, int64_t
             float q[8];
             if constexpr (kPerTensor) {
                 if constexpr (SCHEME == kPerTensorDelayed) key_all = valid && key > key_all ? key : key_all;
+                float d[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(div_by_scale(v[k][e], s_pt, r_pt));
+                for (int e = 0; e < 8; ++e) {
+                    d[e] = div_by_scale(v[k][e], s_pt, r_pt);
+                    q[e] = saturate<FMT, SAT>(d[e]);
+                }
+                if (SCHEME == kPerTensorDelayed && a.count_overflow && valid) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) nov += overflowed<FMT>(v[k][e], d[e]);
+                }
             } else if constexpr (SCHEME == kTileAxis0) {
                 key = row16_max_u32(key);
                 const float sc = scale_from_amax<FMT>(__uint_as_float(key));
@@ -703,7 +747,8 @@ __global__ __launch_bounds__(256) void quantize_flat_kernel(QuantArgs a, int64_t
     } else if constexpr (SCHEME == kPerTensorDelayed) {
         // as in the tiled kernel: the last block to finish folds the per-block
         // maxima and records the grid's amax in the history
-        __shared__ uint32_t last;
+        __shared__ uint32_t last, ov_sum;
+        if (a.count_overflow) add_overflows(a.state, nov, &ov_sum);
         const uint32_t k = block_max_u32_256(key_all, red);
         if (t == 0) last = grid_done(a.keys, a.ctrs, k);
         __syncthreads();

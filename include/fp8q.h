@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 2
+#define FP8Q_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 typedef enum fp8q_status {
@@ -85,6 +85,17 @@ typedef enum fp8q_scaling { FP8Q_CURRENT = 0, FP8Q_DELAYED = 1 } fp8q_scaling;
 
 /* Flags. */
 #define FP8Q_SATURATE 1u   /* clamp finite and infinite overflow to +-fmax instead of NaN / Inf */
+/* Count, into state->overflows, the elements of a delayed-scaling cast that
+ * overflow the format: finite x whose quotient v = RN32(x / s) the
+ * non-saturating cast would turn into NaN (E4M3: |v| > 464, the midpoint
+ * above 448 rounding to the odd-mantissa value past the maximum) or +-Inf
+ * (E5M2: |v| >= 61440, the tie above 57344 rounding to even 2^16); counted
+ * the same way under FP8Q_SATURATE, where such elements are clamped.  This
+ * is how a caller detects the overflow that delayed scaling risks when the
+ * amax grows past its history (the lab page's smoke check [3]).  Only with
+ * DELAYED per-tensor scaling (the count lives in its state); elsewhere
+ * FP8Q_EINVAL. */
+#define FP8Q_COUNT_OVERFLOW 2u
 
 #define FP8Q_HISTORY_LEN 16
 
@@ -92,14 +103,16 @@ typedef enum fp8q_scaling { FP8Q_CURRENT = 0, FP8Q_DELAYED = 1 } fp8q_scaling;
  * Delayed-scaling state, in DEVICE memory, owned by the caller.  Create it
  * zero-filled (an all-zero history is a cold start, which uses the current
  * amax).  The grid-wide amax of a call is folded in the call's reduce
- * workspace; amax_bits and arrive are reserved (keep them zero).  One state
+ * workspace; arrive is reserved (keep it zero).  overflows: after every
+ * delayed call, the number of elements that overflowed the format when the
+ * call had FP8Q_COUNT_OVERFLOW, else 0.  One state
  * must not be used by two calls that may run concurrently.  Saving
  * amax_history and pos checkpoints the recipe.
  */
 typedef struct fp8q_delayed_state {
     float amax_history[FP8Q_HISTORY_LEN]; /* amaxes of earlier steps (ring) */
     int32_t pos;                          /* next ring slot to write */
-    uint32_t amax_bits;                   /* reserved, zero */
+    uint32_t overflows;                   /* overflowing elements of the last call (FP8Q_COUNT_OVERFLOW) */
     uint32_t arrive;                      /* reserved, zero */
     float last_scale;                     /* scale used by the most recent call */
 } fp8q_delayed_state;
@@ -147,8 +160,9 @@ int fp8_amax(const void* x, int hp, int64_t n, float* amax_out,
  * qT: optional (may be NULL) second copy of the codes transposed, [cols, rows]
  *   (the K-major operand of a dgrad or wgrad GEMM).
  * scale_out: required, receives s.  amax_out: optional, receives amax(x).
- * flags: 0 or FP8Q_SATURATE.  ws: fp8q_reduce_workspace_bytes() bytes,
- * zero-filled before its first use (see fp8q_reduce_workspace_bytes).
+ * flags: FP8Q_SATURATE and, with DELAYED, FP8Q_COUNT_OVERFLOW.
+ * ws: fp8q_reduce_workspace_bytes() bytes, zero-filled before its first use
+ * (see fp8q_reduce_workspace_bytes).
  * state: required for DELAYED, ignored for CURRENT.
  * Lab page: scaled_roundtrip; smoke check [3] (delayed vs current).
  */
@@ -299,7 +313,7 @@ typedef struct fp8q_operand {
     int32_t granularity;  /* fp8q_gran */
     int32_t hp;           /* fp8q_hp (autocast) */
     int32_t scaling;      /* fp8q_scaling (autocast, per-tensor) */
-    uint32_t flags;       /* FP8Q_SATURATE (autocast) */
+    uint32_t flags;       /* FP8Q_SATURATE; FP8Q_COUNT_OVERFLOW with DELAYED (autocast) */
     fp8q_delayed_state* state;
     float* scale_out;
     float* amax_out;

@@ -58,6 +58,7 @@ def lib():
         L.orc_philox4x32_10.restype, L.orc_philox4x32_10.argtypes = None, [P, P, P]
         L.orc_sr_word.restype, L.orc_sr_word.argtypes = U32, [U64, U64, U64]
         L.orc_set_threads.restype, L.orc_set_threads.argtypes = None, [I32]
+        L.orc_overflow_count.restype, L.orc_overflow_count.argtypes = I64, [P, I32, I64, F, I32]
         L.orc_max_threads.restype, L.orc_max_threads.argtypes = I32, []
         L.orc_encode_sr.restype, L.orc_encode_sr.argtypes = ctypes.c_uint8, [F, U32, I32, I32]
         L.orc_quantize_per_tensor_sr.restype = None
@@ -145,6 +146,13 @@ def cast(x, s, fmt, saturate=False):
     q = np.empty(x.shape, dtype=np.uint8)
     lib().orc_cast(_ptr(x), hp, x.size, float(s), fmt, int(saturate), _ptr(q))
     return q
+
+
+def overflow_count(x, s, fmt):
+    """Finite elements whose non-saturating cast with scale s overflows the
+    format (E4M3 NaN code, E5M2 Inf code)."""
+    x, hp = _hp(x)
+    return int(lib().orc_overflow_count(_ptr(x), hp, x.size, float(s), fmt))
 
 
 def quantize_per_tensor(x, fmt, saturate=False):

@@ -225,6 +225,25 @@ void orc_quantize_delayed(const void* x, int hp, int64_t n, int fmt, int saturat
     if (amax_out) *amax_out = amax;
 }
 
+/* Overflow count of a cast with scale s: the finite x_i whose non-saturating
+ * code encode(RN32(x_i / s)) is the format's overflow code (E4M3: NaN, as
+ * the format has no infinities; E5M2: +-Inf).  This is what delayed scaling
+ * risks when the amax outgrows its history ([LAB] smoke check [3]); a
+ * saturating cast clamps the same elements. */
+int64_t orc_overflow_count(const void* x, int hp, int64_t n, float s, int fmt)
+{
+    int64_t i, count = 0;
+#pragma omp parallel for reduction(+ : count) schedule(static)
+    for (i = 0; i < n; ++i) {
+        const float xi = load_hp(x, hp, i);
+        uint8_t c;
+        if (!isfinite(xi)) continue;
+        c = orc_cast1(xi, s, fmt, 0);
+        if (fmt == ORC_E4M3 ? (c & 0x7F) == 0x7F : (c & 0x7F) == 0x7C) ++count;
+    }
+    return count;
+}
+
 /* ------------------------------------------------------------------ */
 /* Stochastic rounding of a cast ([BLOG]: the low-precision recipe rounds */
 /* its gradients stochastically; applied here to the 8-bit formats).      */

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_abi_version() == 2
+    assert L.fp8q_abi_version() == 3
     assert L.fp8q_status_string(0) == b"ok"
     for s in range(1, 7):
         assert L.fp8q_status_string(s) not in (b"ok", b"unknown status")
@@ -68,6 +68,14 @@ def test_invalid_arguments_are_rejected_before_any_gpu_call():
                                      None) == fq.EINVAL
     assert L.fp8_quantize_per_tensor(*args, 0, 0, None, fake, None, fake, None, 8, ws, 4096, None) == fq.EINVAL
     assert L.fp8_quantize_per_tensor(*args, 0, 0, None, fake, None, None, None, 0, ws, 4096, None) == fq.EINVAL
+    # overflow count: only with delayed scaling, and only on the per-tensor cast
+    assert L.fp8_quantize_per_tensor(*args, 0, fq.CURRENT, None, fake, None, fake, None, fq.COUNT_OVERFLOW, ws,
+                                     4096, None) == fq.EINVAL
+    assert b"COUNT_OVERFLOW" in L.fp8q_last_error()
+    assert L.fp8_quantize_tile1x128(fake, fq.BF16, 4, 4, 0, 0, fake, None, fake, fq.COUNT_OVERFLOW,
+                                    None) == fq.EINVAL
+    assert L.fp8_quantize_per_tensor_sr(fake, fq.BF16, 4, 4, 1, 1, 0, fake, None, fake, None, fq.COUNT_OVERFLOW,
+                                        ws, 4096, None) == fq.EINVAL
     # misaligned element pointer
     assert L.fp8_amax(P(0x10001), fq.BF16, 10, fake, ws, 4096, None) == fq.EALIGN
     # tiles: bad axis; mx: missing scales
@@ -122,6 +130,9 @@ def test_gemm_validation():
     # delayed scaling is per-tensor only
     Ad = _op(quantized=0, hp=fq.BF16, scaling=fq.DELAYED, granularity=fq.TILE_1x128, state=0x50000)
     assert L.fp8_gemm_scaled_NT(64, 64, 128, R(Ad), R(B), fake, fq.BF16, None, 0, None) == fq.EUNSUPPORTED
+    # an overflow count needs a delayed per-tensor autocast operand
+    Ac = _op(quantized=0, hp=fq.BF16, scaling=fq.CURRENT, flags=fq.COUNT_OVERFLOW)
+    assert L.fp8_gemm_scaled_NT(64, 64, 64, R(Ac), R(B), fake, fq.BF16, None, 0, None) == fq.EINVAL
     # misaligned codes
     Amis = _op(data=0x10008)
     assert L.fp8_gemm_scaled_NT(64, 64, 64, R(Amis), R(B), fake, fq.BF16, None, 0, None) == fq.EALIGN

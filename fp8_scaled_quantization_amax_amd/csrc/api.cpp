@@ -376,7 +376,8 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, i
                             fp8q_delayed_state* state, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
                             unsigned flags, void* ws, size_t ws_bytes, void* stream) {
     int r;
-    if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags, FP8Q_SATURATE | FP8Q_COUNT_OVERFLOW)) != FP8Q_OK) return r;
+    if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags, FP8Q_SATURATE | FP8Q_COUNT_OVERFLOW)) != FP8Q_OK)
+        return r;
     if (scale_out == nullptr) return fail(FP8Q_EINVAL, "scale_out is required");
     if (scaling != FP8Q_CURRENT && scaling != FP8Q_DELAYED) return fail(FP8Q_EINVAL, "unknown scaling %d", scaling);
     if (scaling == FP8Q_DELAYED && state == nullptr) return fail(FP8Q_EINVAL, "delayed scaling needs a state");

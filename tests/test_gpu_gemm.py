@@ -228,6 +228,35 @@ def test_block_scaled_persistent_multi_tile(op):
     assert gemm_close(C[torch.as_tensor(rows, device=C.device)], ref, torch.bfloat16)
 
 
+def test_gemm_beyond_32_bit_offsets():
+    """A GEMM whose A operand spans more than 2^32 bytes (M * K > 2^32), so
+    the persistent kernel's 32-bit buffer offsets do not reach it and the
+    register-staged kernel takes it: sampled rows, those that straddle the
+    2^32-byte offset included, against the oracle."""
+    M, N, K = 262160, 256, 16384
+    assert M * K > 2 ** 32
+    announce("gemm beyond 32-bit offsets", M, N, K)
+    g = torch.Generator(device=dev()).manual_seed(4242)
+    # E4M3 codes with magnitude codes 0x00..0x76 (|v| <= 224) and random signs: no NaN code
+    A = torch.randint(0, 0x77, (M, K), dtype=torch.uint8, device=dev(), generator=g)
+    A |= torch.randint(0, 2, (M, K), dtype=torch.uint8, device=dev(), generator=g) << 7
+    B = torch.randint(0, 0x77, (N, K), dtype=torch.uint8, device=dev(), generator=g)
+    sa = torch.tensor([2.0 ** -10], dtype=torch.float32, device=dev())
+    sb = torch.tensor([2.0 ** -6], dtype=torch.float32, device=dev())
+    C = fq.fp8_gemm_scaled_NT(M, N, K, Q(A, fq.E4M3, sa, fq.PER_TENSOR), Q(B, fq.E4M3, sb, fq.PER_TENSOR),
+                              torch.bfloat16)
+    torch.cuda.synchronize()
+    edge = 2 ** 32 // K   # first row whose bytes start at or past 2^32
+    rows = np.array(sorted(set(sample_rows(M, seed=7).tolist()) | {edge - 1, edge, edge + 1, M - 16}), np.int64)
+    ra = torch.as_tensor(rows, device=dev())
+    oa = A[ra].cpu().numpy()
+    ob = B.cpu().numpy()
+    ref = oracle.gemm_nt(oa, ob, fq.E4M3, fq.E4M3, oracle.Scale("tensor", np.float32(2.0 ** -10)),
+                         oracle.Scale("tensor", np.float32(2.0 ** -6)))
+    del A
+    assert gemm_close(C[ra], ref, torch.bfloat16)
+
+
 # K = 128 or K % 128 != 0: the register-staged kernel; K >= 256 with K % 128 == 0
 # (here 3, 8 and 9 K steps, ragged M and N): the persistent kernel's MX mode.
 @pytest.mark.parametrize("op", ["NT", "NN", "TN"])

@@ -229,3 +229,26 @@ def test_deterministic_reruns():
     r2 = fq.fp8_quantize_per_tensor(x, fq.E4M3, emit_t=True)
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
+
+
+def test_per_tensor_beyond_32_bit_offsets():
+    """Per-tensor current quantization of a bf16 tensor larger than 2^32 bytes,
+    its maximum in the very last element: amax and scale exact, and the codes
+    of sampled rows (both ends included) equal to the oracle's cast."""
+    rows, cols = 65536, 32784
+    assert rows * cols * 2 > 2 ** 32
+    announce("per-tensor beyond 32-bit offsets", rows, cols)
+    g = torch.Generator(device=dev()).manual_seed(99)
+    x = torch.randn((rows, cols), dtype=torch.bfloat16, device=dev(), generator=g)
+    x[-1, -1] = 1000.0
+    q, _, s, a = fq.fp8_quantize_per_tensor(x, fq.E4M3)
+    torch.cuda.synchronize()
+    bits = workloads.bf16_bits(x.cpu())
+    oa = oracle.amax(bits)
+    os_ = oracle.scale_from_amax(oa, fq.E4M3)
+    assert a.item() == oa == 1000.0 and s.item() == os_
+    sample = np.array([0, 1, rows // 2, rows - 2, rows - 1], np.int64)
+    got = q[torch.as_tensor(sample, device=dev())].cpu().numpy()
+    want = oracle.cast(bits[sample], os_, fq.E4M3)
+    assert codes_equal(got, want, fq.E4M3)
+    assert got[-1, -1] == 0x7E   # the maximum encodes to the largest code

@@ -1,0 +1,78 @@
+"""The library enqueues on the caller's stream and keeps no state between
+calls beyond what the caller owns, so its calls run on a side stream and
+inside a captured HIP graph exactly as they run eagerly (bitwise)."""
+import pytest
+import torch
+
+import fp8_scaled_quantization_amax_amd as fq
+import workloads
+from gpu_util import announce, dev
+
+pytestmark = pytest.mark.gpu
+
+AC = fq.GemmOperand.autocast
+Q = fq.GemmOperand.quantized
+
+
+def inputs():
+    A = workloads.normal((528, 1024), 1.0 / 32, 501, torch.bfloat16).to(dev())
+    B = workloads.normal((400, 1024), 1.0 / 32, 502, torch.bfloat16).to(dev())
+    return A, B
+
+
+def test_side_stream_matches_default_stream():
+    announce("side stream")
+    A, B = inputs()
+    q0, _, s0, a0 = fq.fp8_quantize_per_tensor(A, fq.E4M3)
+    C0 = fq.fp8_gemm_scaled_NT(528, 400, 1024, AC(A, fq.E4M3), AC(B, fq.E4M3), torch.bfloat16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev())
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q1, _, s1, a1 = fq.fp8_quantize_per_tensor(A, fq.E4M3)
+        C1 = fq.fp8_gemm_scaled_NT(528, 400, 1024, AC(A, fq.E4M3), AC(B, fq.E4M3), torch.bfloat16)
+    side.synchronize()
+    assert torch.equal(q0, q1) and torch.equal(s0, s1) and torch.equal(a0, a1)
+    assert torch.equal(C0, C1)
+
+
+def test_graph_replays_match_eager():
+    """Quantize (per-tensor current, with a K-major copy) and a pre-quantized
+    GEMM on those codes, captured once and replayed three times with eager
+    library calls in between; every replay equals the eager result."""
+    announce("graph replay")
+    A, B = inputs()
+    ws = fq.reduce_workspace(dev())
+    qb, _, sb, _ = fq.fp8_quantize_per_tensor(B, fq.E4M3)
+    C = torch.empty((528, 400), dtype=torch.bfloat16, device=dev())
+    q = torch.empty((528, 1024), dtype=torch.uint8, device=dev())
+
+    def work():
+        qa, qaT, sa, _ = fq.fp8_quantize_per_tensor(A, fq.E4M3, emit_t=True, ws=ws)
+        q.copy_(qa)
+        fq.fp8_gemm_scaled_NT(528, 400, 1024, Q(qa, fq.E4M3, sa), Q(qb, fq.E4M3, sb), torch.bfloat16, out=C)
+        return qaT
+
+    qT_eager = work().clone()
+    torch.cuda.synchronize()
+    q_eager, C_eager = q.clone(), C.clone()
+    s = torch.cuda.Stream(device=dev())
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        qT_graph = work()
+    other = workloads.normal((256, 512), 4.0, 503, torch.bfloat16).to(dev())
+    for replay in range(3):
+        q.zero_()
+        C.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q, q_eager), replay
+        assert torch.equal(qT_graph, qT_eager), replay
+        assert torch.equal(C, C_eager), replay
+        fq.fp8_quantize_per_tensor(other, fq.E5M2, ws=ws)   # eager work between replays
+        torch.cuda.synchronize()

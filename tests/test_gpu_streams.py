@@ -76,3 +76,68 @@ def test_graph_replays_match_eager():
         assert torch.equal(C, C_eager), replay
         fq.fp8_quantize_per_tensor(other, fq.E5M2, ws=ws)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_delayed_scaling_replayed_graph_follows_the_oracle():
+    """The delayed state lives in device memory, so one captured delayed cast,
+    replayed once per step with that step's data copied into its input
+    buffer, walks the same 17-step sequence (16 warm-up steps, then a
+    40-sigma spike) as the oracle: scale, codes and history at every step."""
+    import numpy as np
+    import oracle
+    from gpu_util import codes_equal, host_input
+    announce("delayed scaling in a graph")
+    shape = (256, 512)
+    steps = list(workloads.delayed_steps(M=shape[0], K=shape[1], steps=17))
+    x_buf = torch.empty(shape, dtype=torch.bfloat16, device=dev())
+    st = fq.DelayedState(dev())
+    ws = fq.reduce_workspace(dev())
+    s = torch.cuda.Stream(device=dev())
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on a throwaway state
+        fq.fp8_quantize_per_tensor(x_buf.zero_(), fq.E4M3, fq.DELAYED, fq.DelayedState(dev()), ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        q, _, sc, _ = fq.fp8_quantize_per_tensor(x_buf, fq.E4M3, fq.DELAYED, st, ws=ws, count_overflow=True)
+    ost = oracle.DelayedState()
+    for t, x, spike in steps:
+        x_buf.copy_(x.to(dev()))
+        graph.replay()
+        torch.cuda.synchronize()
+        oq, os_, _ = oracle.quantize_delayed(host_input(x), fq.E4M3, ost)
+        assert sc.item() == os_, t
+        assert codes_equal(q.cpu().numpy(), oq.reshape(shape), fq.E4M3), t
+        assert np.array_equal(st.history.cpu().numpy(), ost.hist), t
+        assert st.overflows.item() == oracle.overflow_count(host_input(x), os_, fq.E4M3), t
+
+
+def test_concurrent_streams_with_their_own_workspaces():
+    """Two streams running autocast GEMMs and quantize calls at the same time,
+    each with its own workspace: every result equals the eager one."""
+    announce("concurrent streams")
+    A, B = inputs()
+    A2 = (A * 3).contiguous()
+    C_ref = fq.fp8_gemm_scaled_NT(528, 400, 1024, AC(A, fq.E4M3), AC(B, fq.E4M3), torch.bfloat16)
+    C2_ref = fq.fp8_gemm_scaled_NT(528, 400, 1024, AC(A2, fq.E5M2), AC(B, fq.E4M3), torch.bfloat16)
+    q_ref = fq.fp8_quantize_per_tensor(A2, fq.E5M2)[0]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(device=dev()), torch.cuda.Stream(device=dev())
+    need = fq.gemm_workspace_bytes("NT", 528, 400, 1024, AC(A, fq.E4M3), AC(B, fq.E4M3))
+    ws1, ws2 = fq._ws(need, dev()), fq._ws(need, dev())
+    r1, r2 = fq.reduce_workspace(dev()), fq.reduce_workspace(dev())
+    outs1, outs2 = [], []
+    for it in range(8):
+        with torch.cuda.stream(s1):
+            outs1.append(fq.fp8_gemm_scaled_NT(528, 400, 1024, AC(A, fq.E4M3), AC(B, fq.E4M3), torch.bfloat16,
+                                               ws=ws1))
+            outs1.append(fq.fp8_quantize_per_tensor(A2, fq.E5M2, ws=r1)[0])
+        with torch.cuda.stream(s2):
+            outs2.append(fq.fp8_gemm_scaled_NT(528, 400, 1024, AC(A2, fq.E5M2), AC(B, fq.E4M3), torch.bfloat16,
+                                               ws=ws2))
+            outs2.append(fq.fp8_quantize_per_tensor(A2, fq.E5M2, ws=r2)[0])
+    torch.cuda.synchronize()
+    for k in range(0, len(outs1), 2):
+        assert torch.equal(outs1[k], C_ref) and torch.equal(outs2[k], C2_ref)
+        assert torch.equal(outs1[k + 1], q_ref) and torch.equal(outs2[k + 1], q_ref)

@@ -21,7 +21,9 @@
 // from x instead of writing y out and reading it back (2 x 4 bytes per element
 // more HBM traffic): pass 1 takes each block's max |y| as a partial maximum,
 // pass 2 folds the partials into the scale and casts.  With the butterflies,
-// the divisions and the sign draws done twice, the pair is ALU-bound.  A thread owns one 16-row block of 8
+// the divisions and the sign draws done twice, the pair is ALU-heavy, and
+// since a thread takes its unit from load to store with nothing else in
+// flight, load latency shows as well.  A thread owns one 16-row block of 8
 // columns: 16 loads of 16 bytes (bf16) from consecutive rows, 8 transforms of
 // 16 values in registers, 16 stores of 8 codes; neighbouring threads take
 // neighbouring column groups, so every load and store is coalesced.

@@ -36,7 +36,10 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
 // FMA).  Non-finite q0 (x non-finite, or |x/s| beyond fp32) is returned as is:
 // every such quotient encodes to the overflow / NaN code either way.  The
 // sign is restored at the end because the residual steps turn -0 into +0.
+// An infinite scale (an infinite amax) takes x * 0 = x / Inf instead: +-0 for
+// finite x, NaN for infinite x, where the residual steps would form 0 * Inf.
 __host__ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+    if (__builtin_isinf(s)) return x * r;
     const float q0 = x * r;
     if (!(__builtin_fabsf(q0) <= 3.402823466e38f)) return q0;
     float e = __builtin_fmaf(-q0, s, x);

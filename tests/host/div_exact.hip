@@ -14,6 +14,7 @@
 #include "device_common.h"
 
 static inline float f_of(uint32_t b) { float f; std::memcpy(&f, &b, 4); return f; }
+static inline uint32_t bits_of(float f) { uint32_t b; std::memcpy(&b, &f, 4); return b; }
 static inline uint32_t b_of(float f) { uint32_t b; std::memcpy(&b, &f, 4); return b; }
 
 // 1 if the pair differs in a way that could change a code
@@ -57,5 +58,14 @@ int main(int argc, char** argv) {
         for (long long i = 0; i < (1LL << 32); ++i) bad2 += relevant_mismatch(f_of((uint32_t)i), s, r);
     }
     std::printf("all fp32 x %d scales: %ld relevant mismatches\n", nfull, bad2);
-    return (bad == 0 && bad2 == 0) ? 0 : 1;
+    // an infinite scale (an infinite amax): x / Inf exactly, sign of zero included
+    long bad3 = 0;
+    const float inf = f_of(0x7f800000u);
+    for (uint32_t b = 0; b < 65536; ++b) {
+        const float x = f_of(b << 16), want = x / inf, got = fp8q::div_by_scale(x, inf, 1.0f / inf);
+        const bool same = (want != want) ? (got != got) : (bits_of(got) == bits_of(want));
+        bad3 += same ? 0 : 1;
+    }
+    std::printf("bf16 x infinite scale: %ld mismatches\n", bad3);
+    return (bad == 0 && bad2 == 0 && bad3 == 0) ? 0 : 1;
 }

@@ -1,8 +1,9 @@
 """The quantizers divide by the scale with a reciprocal and two FMA residual
 corrections instead of a full IEEE division.  This CPU test compiles that very
 helper (csrc/device_common.h, div_by_scale) as host code and checks it against
-the correctly rounded fp32 quotient: every bf16 input against 2000 scales, and
-every fp32 input against one scale."""
+the correctly rounded fp32 quotient: every bf16 input against 2000 scales,
+every fp32 input against one scale, and every bf16 input against an infinite
+scale (x / Inf: +-0 for finite x, NaN otherwise)."""
 import os
 import subprocess
 
@@ -23,3 +24,4 @@ def test_division_matches_correctly_rounded_quotient():
     assert r.returncode == 0, r.stdout + r.stderr
     assert "bf16 x 2000 scales: 0 relevant mismatches" in r.stdout
     assert "all fp32 x 1 scales: 0 relevant mismatches" in r.stdout
+    assert "bf16 x infinite scale: 0 mismatches" in r.stdout

@@ -69,3 +69,27 @@ def test_degenerate_inputs(name, fmt, dtype):
         q, _, _, _ = fq.fp8_quantize_per_tensor(xd, fmt)
         top = 0x7E if fmt == fq.E4M3 else 0x7B
         assert (q.cpu().numpy() == (0x80 | top)).all()   # -2.5 is the amax: every code is -max
+
+
+@pytest.mark.parametrize("fmt", [fq.E4M3, fq.E5M2])
+@pytest.mark.parametrize("name", list(CASES))
+def test_degenerate_inputs_rowwise_sr_rht(name, fmt):
+    """The same inputs through the rowwise, stochastically rounded and
+    Hadamard-transformed quantizers (bf16 in)."""
+    announce("degenerate rowwise/sr/rht", name, fmt)
+    x = CASES[name].to(torch.bfloat16)
+    xd = x.to(dev())
+    hx = host_input(x)
+    for axis in (0, 1):
+        q, _, sc = fq.fp8_quantize_rowwise(xd, axis, fmt, emit_t=axis == 1)
+        oq, osc = oracle.quantize_rowwise(hx, axis, fmt)
+        assert codes_equal(q.cpu().numpy(), oq.reshape(SHAPE), fmt), axis
+        assert scales_equal(sc.cpu().numpy(), osc), axis
+    q, _, s, a = fq.fp8_quantize_per_tensor_sr(xd, fmt, 1234, 5)
+    oq, os_, oa = oracle.quantize_per_tensor_sr(hx, fmt, 1234, 5)
+    assert scales_equal(s.cpu().numpy(), np.array([os_], np.float32))
+    assert codes_equal(q.cpu().numpy(), oq.reshape(SHAPE), fmt)
+    q, _, s, a = fq.fp8_quantize_per_tensor_rht(xd, fmt, 99)
+    oq, os_, oa = oracle.quantize_per_tensor_rht(hx, fmt, 99)
+    assert scales_equal(s.cpu().numpy(), np.array([os_], np.float32))
+    assert codes_equal(q.cpu().numpy(), oq.reshape(SHAPE), fmt)

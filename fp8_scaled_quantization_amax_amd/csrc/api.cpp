@@ -155,9 +155,17 @@ int plan_gemm(int op, int64_t M, int64_t N, int64_t K, const fp8q_operand* A, co
     const bool arow = A->granularity == FP8Q_ROWWISE, brow = B->granularity == FP8Q_ROWWISE;
     if ((arow || brow) && !((arow || A->granularity == FP8Q_PER_TENSOR) && (brow || B->granularity == FP8Q_PER_TENSOR)))
         return fail(FP8Q_EUNSUPPORTED, "rowwise scaling combines only with rowwise or per-tensor scaling");
+    // A non-empty workspace starts with the reduce region (partial maxima,
+    // per-block keys, completion counters), whatever the shapes and
+    // granularities: its counters then sit at the same place in every call,
+    // so one zero-filled workspace can serve GEMMs of different plans in turn
+    // without a later call's counters landing on codes an earlier one wrote.
+    auto needs_ws = [&](const fp8q_operand* o, bool kcontig) {
+        return !o->quantized || (!kcontig && o->data_kmajor == nullptr);
+    };
     size_t off = 0;
     p.partials_off = 0;
-    bool need_partials = false;
+    if (needs_ws(A, op != kTN) || needs_ws(B, op == kNT)) off = align_up(fp8q::kReduceWsBytes);
     auto plan_one = [&](const fp8q_operand* o, bool kcontig, int64_t R, OperandPlan& q) {
         q = OperandPlan{};
         q.kcontig_stored = kcontig;
@@ -172,15 +180,10 @@ int plan_gemm(int op, int64_t M, int64_t N, int64_t K, const fp8q_operand* A, co
             q.scale_off = off;
             q.scale_bytes = scale_bytes_for(o->granularity, R, K);
             off = align_up(off + q.scale_bytes);
-            if (o->granularity == FP8Q_PER_TENSOR) need_partials = true;
         }
     };
     plan_one(A, op != kTN, M, p.a);
     plan_one(B, op == kNT, N, p.b);
-    if (need_partials) {
-        p.partials_off = off;
-        off = align_up(off + fp8q::kReduceWsBytes);
-    }
     p.total = off;
     return FP8Q_OK;
 }

@@ -718,7 +718,7 @@ static void launch_sm(const GemmArgs& g, int sm, hipStream_t s) {
     else if (sm == kSmRow && fast)
         hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmRow>), dim3(persistent_grid()), dim3(kThreads), 0, s, g,
                            ntm, ntn);
-    else if (sm == kSmMx && fast && g.K % 512 == 0)
+    else if (sm == kSmMx && fast && g.K % 512 == 0 && (uintptr_t)g.sa.s % 16 == 0 && (uintptr_t)g.sb.s % 16 == 0)
         hipLaunchKernelGGL((gemm_pt_kernel<FA, FB, OUT, kSmMx>), dim3(persistent_grid()), dim3(kThreads), 0, s, g,
                            ntm, ntn);
     else if (sm == kSmPerTensor)

@@ -30,6 +30,10 @@ namespace fp8q {
 // converter then overflows like any other value); NaN and Inf pass unchanged.
 // |v| = M 2^(e - 23) with the 24-bit significand M; the grid spacing is
 // 2^D with D = max(e, emin) - mantissa bits, so |v| / 2^D = M / 2^shift.
+// Where the round-to-nearest cast of v is finite (|v| <= 464 for E4M3, the
+// tie above 448 rounding down to it; |v| < 61440 for E5M2) the result is
+// capped at fmax: current scaling leaves the amax element an ulp or two above
+// fmax, and rounding it up to the next step would overflow.
 template <int FMT>
 __device__ __forceinline__ float sr_round(float v, uint32_t r) {
     constexpr int MB = FMT == FP8Q_E4M3 ? 3 : 2;
@@ -51,7 +55,10 @@ __device__ __forceinline__ float sr_round(float v, uint32_t r) {
         frac32 = M >> (shift - 32);
     }
     const uint32_t up = r > 0xffffffffu - frac32 ? 1u : 0u;   // r + frac32 >= 2^32
-    const float mag = (float)(n + up) * __uint_as_float((uint32_t)(D + 127) << 23);
+    float mag = (float)(n + up) * __uint_as_float((uint32_t)(D + 127) << 23);
+    const float av = __uint_as_float(ab);
+    const bool rne_finite = FMT == FP8Q_E4M3 ? av <= 464.0f : av < 61440.0f;
+    if (rne_finite && mag > fmt_max<FMT>()) mag = fmt_max<FMT>();
     return __builtin_copysignf(mag, v);
 }
 

@@ -2,10 +2,10 @@
 
 `FP8Matmul` is y = x . w^T with both GEMM inputs quantized to E4M3 in the
 forward and the output gradient quantized to E5M2 in the backward, each with
-its per-tensor current scale.  Accumulation and outputs stay fp32, and the
-fp32 master weights the optimizer updates are never stored in FP8.  It
-follows the "fp8_parity.py" lab page: the class FP8Matmul and the small-MLP
-training of its smoke check [5].
+its per-tensor current scale.  Products accumulate in fp32; the optimizer
+holds and updates fp32 weights, and only each call's GEMM inputs are 8-bit.
+What is computed follows the "fp8_parity.py" lab page: class FP8Matmul and
+the small-MLP training run of its smoke check [5].
 
 How the library is used:
 
@@ -148,28 +148,39 @@ def fp8_matmul(x, w, recipe="tensorwise", sr=None, rht=None):
     return FP8Matmul.apply(x, w, sr, rht)
 
 
+def stack_forward(weights, x, matmul):
+    """x through a stack of bias-free linears, relu between consecutive ones:
+    h_0 = x, h_{j+1} = matmul(act(h_j), W_j, j) with act = relu for j > 0."""
+    h = x
+    for j, w in enumerate(weights):
+        h = matmul(torch.relu(h) if j else h, w, j)
+    return h
+
+
 def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None,
               wgrad_rht_seed=None):
-    """The lab page's check-[5] loop: the 2-layer MLP relu(X W1^T) W2^T is fitted
-    to Y by mean squared error with AdamW(lr), with every matmul either FP8
-    (`fp8_matmul` with `recipe`; with grad_sr_seed, output gradients rounded
-    stochastically, offset 2 step + layer; with wgrad_rht_seed, Hadamard-transformed
-    wgrad operands, seed wgrad_rht_seed + 2 step + layer) or plain fp32.  X, Y, W1 and W2 are device tensors; the
-    weights are copied and left unchanged.  Returns the list of per-step
-    losses (floats, read once at the end)."""
-    W1 = W1.detach().clone().requires_grad_()
-    W2 = W2.detach().clone().requires_grad_()
-    opt = torch.optim.AdamW([W1, W2], lr=lr)
-    def mm(a, b, t, j):
+    """Training run of the lab page's smoke check [5]: the two-linear stack
+    [W1, W2] is fitted to Y by mean squared error under AdamW(lr), each matmul
+    FP8 (`fp8_matmul` with `recipe`; grad_sr_seed: output gradients rounded
+    stochastically at stream offset 2 t + j for step t, linear j;
+    wgrad_rht_seed: Hadamard-transformed wgrad operands with seed
+    wgrad_rht_seed + 2 t + j) or plain fp32.  X, Y, W1, W2 are device tensors;
+    the weights are copied, the inputs left unchanged.  Returns the per-step
+    losses (floats, read back once at the end)."""
+    weights = [w.detach().clone().requires_grad_() for w in (W1, W2)]
+    opt = torch.optim.AdamW(weights, lr=lr)
+
+    def matmul_at(t):
         if not fp8:
-            return a @ b.T
-        return fp8_matmul(a, b, recipe, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j),
-                          None if wgrad_rht_seed is None else wgrad_rht_seed + 2 * t + j)
-    losses = []
-    for t in range(steps):
-        loss = ((mm(torch.relu(mm(X, W1, t, 0)), W2, t, 1) - Y) ** 2).mean()
-        opt.zero_grad()
+            return lambda a, b, j: a @ b.T
+        return lambda a, b, j: fp8_matmul(a, b, recipe, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j),
+                                          None if wgrad_rht_seed is None else wgrad_rht_seed + 2 * t + j)
+
+    def step(t):
+        opt.zero_grad(set_to_none=True)
+        loss = torch.nn.functional.mse_loss(stack_forward(weights, X, matmul_at(t)), Y)
         loss.backward()
         opt.step()
-        losses.append(loss.detach())
-    return [float(v) for v in torch.stack(losses).cpu()]
+        return loss.detach()
+
+    return [float(v) for v in torch.stack([step(t) for t in range(steps)]).cpu()]

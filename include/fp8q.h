@@ -345,9 +345,14 @@ size_t fp8_gemm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K,
  * broadcast).  ROWWISE operands must be pre-quantized (autocast with ROWWISE
  * returns FP8Q_EUNSUPPORTED).
  * ws: fp8_gemm_workspace_bytes(...) bytes (may be NULL when that is 0),
- * zero-filled before its first use: autocast operands reduce in it, and its
- * completion counters must start at zero (every call leaves them at zero).
- * Calls that may overlap on the device must not share a workspace.
+ * 256-byte aligned, zero-filled before its first use: autocast operands
+ * reduce in it, and its completion counters must start at zero (every call
+ * leaves them at zero).  A non-empty workspace always begins with the
+ * reduction region (fp8q_reduce_workspace_bytes() bytes, counters included),
+ * and staged codes and scales follow it, so one zero-filled workspace as
+ * large as each call needs may serve GEMMs of different shapes and
+ * granularities in turn.  Calls that may overlap on the device must not
+ * share a workspace.
  */
 int fp8_gemm_scaled_NT(int64_t M, int64_t N, int64_t K, const fp8q_operand* A,
                        const fp8q_operand* B, void* C, int c_dtype,

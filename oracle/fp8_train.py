@@ -10,8 +10,8 @@ page's FP8Matmul written on the oracle's own definitions:
   rounded once to fp32.
 
 The page multiplies dequantized fp32 tensors (xq @ wq.T).  That is the same
-product up to fp32 summation order.  `train_mlp` is the page's check-[5]
-loop on the CPU.
+product up to fp32 summation order.  `train_mlp` runs the check-[5] training
+on the CPU.
 """
 import numpy as np
 import torch
@@ -92,23 +92,29 @@ class OracleFP8MatmulRowwise(torch.autograd.Function):
 
 def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None,
               wgrad_rht_seed=None):
-    """Fit relu(X W1^T) W2^T to Y by mean squared error with AdamW(lr), every
-    matmul either the oracle's FP8 matmul of `recipe` or plain fp32; returns
-    the per-step losses."""
-    W1 = W1.detach().clone().requires_grad_()
-    W2 = W2.detach().clone().requires_grad_()
-    opt = torch.optim.AdamW([W1, W2], lr=lr)
-    def mm(a, b, t, j):
-        if not fp8:
-            return a @ b.T
-        if recipe == "rowwise":
-            return OracleFP8MatmulRowwise.apply(a, b)
-        return OracleFP8Matmul.apply(a, b, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j),
-                                     None if wgrad_rht_seed is None else wgrad_rht_seed + 2 * t + j)
+    """The smoke-check [5] training run on the CPU: the stack [W1, W2] (relu
+    between the two linears) fitted to Y by mean squared error under
+    AdamW(lr), every matmul the oracle's FP8 matmul of `recipe` or plain
+    fp32; returns the per-step losses."""
+    weights = [w.detach().clone().requires_grad_() for w in (W1, W2)]
+    opt = torch.optim.AdamW(weights, lr=lr)
+
+    def fp8_mm(t):
+        def mm(a, b, j):
+            if recipe == "rowwise":
+                return OracleFP8MatmulRowwise.apply(a, b)
+            return OracleFP8Matmul.apply(a, b, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j),
+                                         None if wgrad_rht_seed is None else wgrad_rht_seed + 2 * t + j)
+        return mm
+
     losses = []
     for t in range(steps):
-        loss = ((mm(torch.relu(mm(X, W1, t, 0)), W2, t, 1) - Y) ** 2).mean()
-        opt.zero_grad()
+        mm = fp8_mm(t) if fp8 else (lambda a, b, j: a @ b.T)
+        h = X
+        for j, w in enumerate(weights):
+            h = mm(torch.relu(h) if j else h, w, j)
+        loss = torch.nn.functional.mse_loss(h, Y)
+        opt.zero_grad(set_to_none=True)
         loss.backward()
         opt.step()
         losses.append(loss.item())

@@ -293,12 +293,16 @@ uint32_t orc_sr_word(uint64_t seed, uint64_t offset, uint64_t i)
  * (2^(max(floor(log2|v|), 1 - bias) - mantissa bits)); with
  * f = |v| / D - n, the magnitude becomes (n + 1) D when
  * r + floor(f * 2^32) >= 2^32 -- probability floor(f * 2^32) / 2^32 for a
- * uniform r -- and n D otherwise.  The sign is kept and the result encoded
- * as a cast is (so a step past the largest finite value overflows like a
- * cast).  NaN and +-Inf are encoded unchanged. */
+ * uniform r -- and n D otherwise.  Where the round-to-nearest cast of v is
+ * finite, the magnitude is capped at the format maximum: a v just above the
+ * maximum (current scaling puts the amax element within an ulp or two of
+ * it) must not round up to a step past it and overflow.  Where that cast
+ * overflows, the stochastic result is encoded as it stands (a step past the
+ * maximum then overflows like a cast).  The sign is kept.  NaN and +-Inf
+ * are encoded unchanged. */
 uint8_t orc_encode_sr(float v, uint32_t r, int fmt, int saturate)
 {
-    double a, D, n, f;
+    double a, D, n, f, mag;
     uint64_t frac32;
     int e;
     if (isnan(v) || isinf(v)) return orc_encode(v, fmt, saturate);
@@ -314,7 +318,13 @@ uint8_t orc_encode_sr(float v, uint32_t r, int fmt, int saturate)
     f = a / D - n;
     frac32 = (uint64_t)floor(ldexp(f, 32));
     if ((uint64_t)r + frac32 >= ((uint64_t)1 << 32)) n += 1.0;
-    return orc_encode((float)copysign(n * D, (double)v), fmt, saturate);
+    mag = n * D;
+    if (mag > orc_fmax(fmt)) {
+        const uint8_t rne = orc_encode(v, fmt, 0);
+        const int rne_finite = fmt == ORC_E4M3 ? (rne & 0x7F) != 0x7F : (rne & 0x7F) < 0x7C;
+        if (rne_finite) mag = orc_fmax(fmt);
+    }
+    return orc_encode((float)copysign(mag, (double)v), fmt, saturate);
 }
 
 /* Per-tensor current scaling with a stochastically rounded cast: amax and

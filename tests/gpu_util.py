@@ -82,3 +82,16 @@ def sample_rows(M, seed, tile=256, n_tiles=6, n_rand=12):
         rows.add(min(M - 1, int(t) * tile + tile - 1))
     rows.update(int(r) for r in rng.integers(0, M, n_rand))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def contract_rows(M, seed, tile=128, n_rand=256):
+    """The full-size sample of output rows: the first and last row of every
+    `tile`-row M tile, plus n_rand seeded random rows (all N columns are
+    compared)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for t0 in range(0, M, tile):
+        rows.add(t0)
+        rows.add(min(M, t0 + tile) - 1)
+    rows.update(int(r) for r in rng.choice(M, size=min(n_rand, M), replace=False))
+    return np.array(sorted(rows), dtype=np.int64)

@@ -12,7 +12,7 @@ import torch
 import fp8_scaled_quantization_amax_amd as fq
 import oracle
 import workloads
-from gpu_util import announce, dev, gemm_close, host_input, sample_rows
+from gpu_util import announce, contract_rows, dev, gemm_close, host_input, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -329,26 +329,44 @@ def test_full_attn_out_prequantized_and_autocast():
     assert torch.equal(C, Ca)
 
 
+def nt_form(op, oqa, oqb, osa, osb):
+    """The oracle's operands of op in the NT form: codes K-contiguous ([M, K],
+    [N, K]) and the scales indexed the same way (a weight's 128x128 block
+    scales, stored [K/128, N/128] for dgrad, transposed with it).  The layouts
+    agree exactly (the oracle's NT = NN = TN pin)."""
+    if not kcontig(op, "A"):
+        oqa = np.ascontiguousarray(oqa.T)
+    if not kcontig(op, "B"):
+        oqb = np.ascontiguousarray(oqb.T)
+    if osb.kind == "blockT":
+        osb = oracle.Scale("block", np.ascontiguousarray(osb.arr.T), kblk=osb.kblk, rblk=osb.rblk)
+    return oqa, oqb, osa, osb
+
+
 @pytest.mark.parametrize("gemm", workloads.layer_gemms(), ids=lambda g: g[0])
 def test_full_layer_gemm_sampled(gemm):
     """Each of the 12 layer GEMMs at full size (operands ~ N(0,1)/sqrt(K)),
     per-tensor current scaling, fprop E4M3 x E4M3, dgrad and wgrad E5M2 x E4M3,
-    autocast, bf16 out, on sampled output rows."""
+    autocast, bf16 out -- the benchmark's launch configuration -- on the first
+    and last row of every 128-row M tile and 256 random rows, all N columns.
+    The same GEMM on pre-quantized codes gives bitwise the same output."""
     name, op, M, N, K = gemm
     announce("full layer", name, op, M, N, K)
     A, B = workloads.gemm_operands(op, M, N, K, seed=4000 + zlib.crc32(name.encode()) % 1000, device=dev())
     fa = fq.E4M3 if op == "NT" else fq.E5M2
     C = GEMM[op](M, N, K, AC(A, fa), AC(B, fq.E4M3))
+    qa, qaT, sa, _ = fq.fp8_quantize_per_tensor(A, fa, emit_t=not kcontig(op, "A"))
+    qb, qbT, sb, _ = fq.fp8_quantize_per_tensor(B, fq.E4M3, emit_t=not kcontig(op, "B"))
+    Cp = GEMM[op](M, N, K, Q(qa, fa, sa, kmajor=qaT), Q(qb, fq.E4M3, sb, kmajor=qbT))
+    assert torch.equal(C, Cp)
+    del Cp, qa, qaT, qb, qbT
     oqa, osa, _ = oracle.quantize_per_tensor(host_input(A), fa)
     oqb, osb, _ = oracle.quantize_per_tensor(host_input(B), fq.E4M3)
-    rows = sample_rows(M, 2, n_tiles=3, n_rand=4)
-    # the oracle's NT form on K-contiguous copies (layouts agree exactly: oracle pin)
-    oqa, oqb = oqa.reshape(A.shape), oqb.reshape(B.shape)
-    if not kcontig(op, "A"):
-        oqa = np.ascontiguousarray(oqa.T)
-    if not kcontig(op, "B"):
-        oqb = np.ascontiguousarray(oqb.T)
-    ref = oracle.gemm_nt(oqa, oqb, fa, fq.E4M3, oracle.Scale("tensor", osa), oracle.Scale("tensor", osb), rows=rows)
+    assert sa.item() == osa and sb.item() == osb
+    oqa, oqb, sa_o, sb_o = nt_form(op, oqa.reshape(A.shape), oqb.reshape(B.shape), oracle.Scale("tensor", osa),
+                                   oracle.Scale("tensor", osb))
+    rows = contract_rows(M, 2)
+    ref = oracle.gemm_nt(oqa, oqb, fa, fq.E4M3, sa_o, sb_o, rows=rows)
     assert gemm_close(C[torch.from_numpy(rows).to(dev())], ref, torch.bfloat16)
 
 
@@ -365,12 +383,14 @@ def mx_codes(op, A, B, fa, fb):
 
 
 @pytest.mark.parametrize("recipe", ["block", "mx"])
-@pytest.mark.parametrize("gemm", [g for g in workloads.layer_gemms() if g[0].startswith("attn_out")],
-                         ids=lambda g: g[0])
-def test_full_attn_out_granular_sampled(gemm, recipe):
-    """The attention-output GEMMs at full size in the benchmark's block-scaled
-    and MX32 recipes (N(0,1) operands with 1% of rows x1e3; fprop E4M3 x E4M3,
-    dgrad / wgrad E5M2 x E4M3; bf16 out), on sampled output rows."""
+@pytest.mark.parametrize("gemm", workloads.layer_gemms(), ids=lambda g: g[0])
+def test_full_layer_granular_sampled(gemm, recipe):
+    """All 12 layer GEMMs at full size in the benchmark's block-scaled recipe
+    (activations / gradients 1x128 along K, weights 128x128, both wgrad
+    operands 128x1 along tokens) and its MX32 recipe (E8M0 per 32 along K),
+    on N(0,1) operands with 1% of rows x1e3; fprop E4M3 x E4M3, dgrad / wgrad
+    E5M2 x E4M3; bf16 out.  Checked on the first and last row of every
+    128-row M tile and 256 random rows, all N columns."""
     name, op, M, N, K = gemm
     announce("full granular", recipe, name, op, M, N, K)
     A, B = workloads.gemm_operands(op, M, N, K, seed=7000 + zlib.crc32(name.encode()) % 1000, std=1.0,
@@ -378,7 +398,102 @@ def test_full_attn_out_granular_sampled(gemm, recipe):
     fa, fb = (fq.E4M3, fq.E4M3) if op == "NT" else (fq.E5M2, fq.E4M3)
     codes = block_scaled_codes if recipe == "block" else mx_codes
     oa, ob, oqa, oqb, osa, osb = codes(op, A, B, fa, fb)
-    rows = sample_rows(M, 3, n_tiles=3, n_rand=4)
-    ref = OGEMM[op](oqa, oqb, fa, fb, osa, osb, rows=rows)
     C = GEMM[op](M, N, K, oa, ob, torch.bfloat16)
+    del oa, ob, A, B
+    oqa, oqb, osa, osb = nt_form(op, oqa, oqb, osa, osb)
+    rows = contract_rows(M, 3)
+    ref = oracle.gemm_nt(oqa, oqb, fa, fb, osa, osb, rows=rows)
     assert gemm_close(C[torch.as_tensor(rows, device=C.device)], ref, torch.bfloat16)
+
+
+def test_full_attn_out_delayed_autocast_spike():
+    """The attention-output GEMM at full size (A [15872, 4096] activations,
+    B [4096, 4096] weight, ~ N(0,1)/64) with delayed scaling of A inside the
+    call: 16 warm-up steps fill the 16-entry history, and the 17th step's
+    activation carries one 40-sigma element.  Its scale comes from the
+    history, so that element overflows E4M3 (NaN): the spike's output row is
+    NaN and no other row is; the history, scales and the sampled rows of the
+    cold-start and spike steps match the oracle."""
+    M, K, N = workloads.M_TOKENS, workloads.HIDDEN, workloads.HIDDEN
+    announce("full delayed autocast", M, N, K)
+    st = fq.DelayedState(dev())
+    ost = oracle.DelayedState()
+    _, B = workloads.attn_out_operands()
+    qb, _, sb, oqb, osb = quantize_pt(B, fq.E4M3, False)
+    ws = torch.zeros(fq.gemm_workspace_bytes("NT", M, N, K, AC(B.to(dev()), fq.E4M3, scaling=fq.DELAYED, state=st),
+                                             Q(qb, fq.E4M3, sb)), dtype=torch.uint8, device=dev())
+    rows = contract_rows(M, 5)
+    for t, x, spike in workloads.delayed_steps(M=M, K=K, steps=17):
+        xd = x.to(dev())
+        C = fq.fp8_gemm_scaled_NT(M, N, K, AC(xd, fq.E4M3, scaling=fq.DELAYED, state=st), Q(qb, fq.E4M3, sb),
+                                  torch.bfloat16, ws=ws)
+        oqa, osa, _ = oracle.quantize_delayed(host_input(x), fq.E4M3, ost)
+        assert st.last_scale.item() == osa, t
+        assert np.array_equal(st.history.cpu().numpy(), ost.hist) and st.pos.item() == ost.pos[0], t
+        if t in (0, 16):
+            r = rows if spike is None else np.union1d(rows, [spike[0]])
+            ref = oracle.gemm_nt(oqa.reshape(M, K), oqb, 0, 0, oracle.Scale("tensor", osa),
+                                 oracle.Scale("tensor", osb), rows=r)
+            assert gemm_close(C[torch.from_numpy(r).to(dev())], ref, torch.bfloat16), t
+        if spike is not None:
+            nan_rows = torch.isnan(C.float()).any(dim=1).nonzero().flatten().cpu().tolist()
+            assert nan_rows == [spike[0]]
+            assert torch.isnan(C[spike[0]].float()).all()
+
+
+def test_workspace_reused_across_shapes_delayed():
+    """One zero-filled workspace serves GEMMs of two different plans in turn
+    for five steps: a dgrad with a delayed-autocast A and a pre-quantized B
+    that is transposed into the workspace, and an fprop of another shape with
+    delayed autocast on both operands.  The outputs equal calls with fresh
+    workspaces bitwise, and every delayed state walks the oracle's history."""
+    announce("workspace reuse across plans")
+    dgrad = ("NN", 1040, 784, 384)
+    fprop = ("NT", 528, 400, 656)
+    Ag, Bw = workloads.gemm_operands(*dgrad, seed=8800)
+    Ax, Bx = workloads.gemm_operands(*fprop, seed=8810)
+    qw, _, sw, _ = fq.fp8_quantize_per_tensor(Bw.to(dev()), fq.E4M3)
+    states = {k: (fq.DelayedState(dev()), fq.DelayedState(dev()), oracle.DelayedState()) for k in ("g", "x", "w")}
+
+    def operands(step, which):   # which = 0: shared workspace's states, 1: the fresh ones'
+        g = (Ag.float() * (1.0 + 0.25 * step)).to(torch.bfloat16)
+        x = (Ax.float() * (1.0 - 0.125 * step)).to(torch.bfloat16)
+        dl = lambda t, fmt, k: AC(t.to(dev()), fmt, scaling=fq.DELAYED, state=states[k][which])
+        return (g, x), ((dl(g, fq.E5M2, "g"), Q(qw, fq.E4M3, sw)), (dl(x, fq.E4M3, "x"), dl(Bx, fq.E4M3, "w")))
+
+    _, ((a0, b0), (a1, b1)) = operands(0, 0)
+    need = max(fq.gemm_workspace_bytes(*dgrad, a0, b0), fq.gemm_workspace_bytes(*fprop, a1, b1))
+    shared = torch.zeros(need, dtype=torch.uint8, device=dev())
+    for step in range(5):
+        (g, x), shared_ops = operands(step, 0)
+        _, fresh_ops = operands(step, 1)
+        for (op, M, N, K), (oa, ob), (fa2, fb2) in zip((dgrad, fprop), shared_ops, fresh_ops):
+            C1 = GEMM[op](M, N, K, oa, ob, torch.float32, ws=shared)
+            C2 = GEMM[op](M, N, K, fa2, fb2, torch.float32)
+            assert torch.equal(C1, C2), (step, op)
+        for k, t, fmt in (("g", g, fq.E5M2), ("x", x, fq.E4M3), ("w", Bx, fq.E4M3)):
+            oracle.quantize_delayed(host_input(t), fmt, states[k][2])
+            assert np.array_equal(states[k][0].history.cpu().numpy(), states[k][2].hist), (step, k)
+            assert states[k][0].pos.item() == states[k][2].pos[0]
+
+
+def test_mx_misaligned_scales():
+    """MX32 scales at an address that is not 16-byte aligned take the general
+    kernel (the persistent one loads them 16 bytes at a time): same result
+    as with aligned scales, within tolerance of the oracle."""
+    op, M, N, K = "NT", 528, 400, 1024
+    announce("mx misaligned scales")
+    A, B = block_operands(op, M, N, K, seed=777)
+    oa, ob, oqa, oqb, osa, osb = mx_codes(op, A, B, fq.E4M3, fq.E4M3)
+    ea, eb = oa.keep[2], ob.keep[2]
+    bufa = torch.empty(ea.numel() + 16, dtype=torch.uint8, device=dev())
+    bufb = torch.empty(eb.numel() + 16, dtype=torch.uint8, device=dev())
+    ea1 = bufa[1:1 + ea.numel()].view(ea.shape)
+    eb1 = bufb[3:3 + eb.numel()].view(eb.shape)
+    ea1.copy_(ea)
+    eb1.copy_(eb)
+    assert ea1.data_ptr() % 16 != 0 and eb1.data_ptr() % 16 != 0
+    ref = oracle.gemm_nt(oqa, oqb, 0, 0, osa, osb)
+    C = GEMM[op](M, N, K, oa, ob, torch.float32)
+    C1 = GEMM[op](M, N, K, Q(oa.keep[0], fq.E4M3, ea1, fq.MX32), Q(ob.keep[0], fq.E4M3, eb1, fq.MX32), torch.float32)
+    assert gemm_close(C, ref, torch.float32) and gemm_close(C1, ref, torch.float32)

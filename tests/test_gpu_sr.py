@@ -61,3 +61,26 @@ def test_sr_full_size_gradient():
     announce("sr full size")
     g = workloads.normal((workloads.M_TOKENS, workloads.HIDDEN), 1.0, 9300, torch.bfloat16)
     check_sr(g, fq.E5M2, seed=2024, offset=17, emit_t=True)
+
+
+@pytest.mark.parametrize("fmt", [fq.E4M3, fq.E5M2], ids=["e4m3", "e5m2"])
+def test_sr_amax_element_stays_finite(fmt):
+    """The amax element's quotient lands one ulp above fmax and its word would
+    round it up: the code is the largest finite one, on the GPU as in the
+    oracle (a step past fmax would be NaN / Inf)."""
+    import sr_search
+    fmax = 448.0 if fmt == fq.E4M3 else 57344.0
+    a = sr_search.bf16_amax_one_ulp_above(fmax)
+    s = np.float32(a) / np.float32(fmax)
+    v = float(np.float32(a) / s)
+    D = 32.0 if fmt == fq.E4M3 else 8192.0
+    frac32 = int(np.floor((v / D - np.floor(v / D)) * 2.0 ** 32))
+    seed = 0x5EED
+    off = sr_search.find_offset(seed, 0, (1 << 32) - frac32)
+    assert off is not None and oracle.sr_word(seed, off, 0) >= (1 << 32) - frac32
+    announce("sr amax element", fmt, off)
+    x = torch.from_numpy((np.random.default_rng(12).standard_normal(4096) * 0.25).astype(np.float32))
+    x[0] = a
+    x = x.to(torch.bfloat16).reshape(16, 256)
+    q = check_sr(x, fmt, seed, off)
+    assert int(q[0, 0].item()) == (0x7E if fmt == fq.E4M3 else 0x7B)

@@ -100,3 +100,63 @@ def test_quantize_sr_against_round_to_nearest(orc, fmt):
     hi = g[np.minimum(lo_i + 1, len(g) - 1)] * np.sign(v)
     assert np.all((got == lo) | (got == hi))
     assert np.any(q != q0)
+
+
+MAXCODE = {E4M3: 0x7E, E5M2: 0x7B}
+FMAX = {E4M3: 448.0, E5M2: 57344.0}
+
+
+@pytest.mark.parametrize("ctr,key,expect", [
+    ((0, 0, 0, 0), (0, 0), (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+    ((0xffffffff,) * 4, (0xffffffff,) * 2, (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+    ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+     (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+])
+def test_search_generator_known_answers(ctr, key, expect):
+    """The numpy generator the edge-case search uses meets the same published vectors."""
+    import sr_search
+    assert tuple(int(w) for w in sr_search.philox4x32_10(*ctr, *key)) == expect
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_sr_caps_at_fmax_where_round_to_nearest_is_finite(orc, fmt):
+    """A quotient one ulp above fmax (where current scaling can put the amax
+    element) never rounds up past fmax, whatever the word; so does the largest
+    value whose round-to-nearest cast is finite.  Past that limit the
+    stochastic result overflows as the cast does."""
+    above = float(np.nextafter(np.float32(FMAX[fmt]), np.float32(np.inf)))
+    last_finite = 464.0 if fmt == E4M3 else float(np.nextafter(np.float32(61440.0), np.float32(0)))
+    first_over = float(np.nextafter(np.float32(464.0), np.float32(np.inf))) if fmt == E4M3 else 61440.0
+    ovf = 0x7F if fmt == E4M3 else 0x7C
+    for v in (above, last_finite):
+        assert orc.encode(v, fmt) == MAXCODE[fmt]
+        for sign in (1.0, -1.0):
+            for r in (0, 1 << 31, 0xffffffff):
+                assert orc.encode_sr(sign * v, r, fmt) == MAXCODE[fmt] | (0x80 if sign < 0 else 0)
+    assert orc.encode(first_over, fmt) & 0x7F == ovf
+    assert orc.encode_sr(first_over, 0xffffffff, fmt) & 0x7F == ovf
+    assert orc.encode_sr(first_over, 0, fmt) == MAXCODE[fmt]
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_sr_amax_element_stays_finite(orc, fmt):
+    """Per-tensor current scaling of a bf16 tensor whose amax element is cast
+    from one ulp above fmax, with a stream offset whose word for that element
+    would round it up: the element's code is the largest finite code."""
+    import sr_search
+    a = sr_search.bf16_amax_one_ulp_above(FMAX[fmt])
+    assert a is not None
+    s = np.float32(a) / np.float32(FMAX[fmt])
+    v = np.float32(a) / s
+    D = 32.0 if fmt == E4M3 else 8192.0          # grid spacing at fmax
+    frac32 = int(np.floor((float(v) / D - np.floor(float(v) / D)) * 2.0 ** 32))
+    assert frac32 > 0
+    seed = 0x5EED
+    off = sr_search.find_offset(seed, 0, (1 << 32) - frac32)
+    assert off is not None and orc.sr_word(seed, off, 0) >= (1 << 32) - frac32
+    x = (np.random.default_rng(12).standard_normal(4096) * 0.25).astype(np.float32)
+    x[0] = a
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q, s_o, a_o = orc.quantize_per_tensor_sr(bits, fmt, seed=seed, offset=off)
+    assert a_o == a and s_o == s
+    assert q[0] == MAXCODE[fmt]

@@ -62,6 +62,7 @@ def lib():
             "fp8q_reduce_workspace_bytes": (SZ, []),
             "fp8_amax": (I, [P, I, I64, P, P, SZ, P]),
             "fp8_quantize_per_tensor": (I, [P, I, I64, I64, I, I, P, P, P, P, P, U, P, SZ, P]),
+            "fp8_quantize_per_tensor_noalloc": (I, [P, I, I64, I64, I, I, P, P, P, P, P, U, P]),
             "fp8_quantize_tile1x128": (I, [P, I, I64, I64, I, I, P, P, P, U, P]),
             "fp8_quantize_block128x128": (I, [P, I, I64, I64, I, P, P, P, U, P]),
             "fp8_quantize_mx32": (I, [P, I, I64, I64, I, I, P, P, P, U, P]),
@@ -189,6 +190,28 @@ def fp8_quantize_per_tensor(x, fmt=E4M3, scaling=CURRENT, state=None, emit_t=Fal
                                          _ptr(scale), _ptr(amax),
                                          (SATURATE if saturate else 0) | (COUNT_OVERFLOW if count_overflow else 0),
                                          _ptr(ws), ws.numel(), _stream()))
+    return q, qT, scale, amax
+
+
+def fp8_quantize_per_tensor_noalloc(x, fmt=E4M3, scaling=CURRENT, state=None, emit_t=False, saturate=False,
+                                    count_overflow=False, out=None):
+    """fp8_quantize_per_tensor with the library's own device scratch in place of a
+    workspace; returns (q, qT, scale, amax).  out = (q, qT, scale, amax) tensors
+    to write into (qT may be None), so that the call itself allocates nothing."""
+    hp = _hp(x)
+    rows, cols = _rows_cols(x)
+    if out is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if emit_t else None
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        q, qT, scale, amax = out
+    st = state.ptr() if state is not None else None
+    _check(lib().fp8_quantize_per_tensor_noalloc(_ptr(x), hp, rows, cols, fmt, scaling, st, _ptr(q), _ptr(qT),
+                                                 _ptr(scale), _ptr(amax),
+                                                 (SATURATE if saturate else 0) |
+                                                 (COUNT_OVERFLOW if count_overflow else 0), _stream()))
     return q, qT, scale, amax
 
 

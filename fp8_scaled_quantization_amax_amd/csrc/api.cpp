@@ -71,6 +71,41 @@ int launched(hipError_t e, const char* what) {
     return FP8Q_OK;
 }
 
+// Scratch of fp8_quantize_per_tensor_noalloc, for callers that cannot
+// allocate: the reduce region (partial maxima, per-block keys, completion
+// counters) in device memory the library owns.  Every device the library
+// runs on holds its own copy, at its own address, until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels and copies take the address from scratch_address().
+constexpr size_t kScratchBytes = 64 * 1024;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's scratch (the current device must be
+// valid), looked up once per device with that device current.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(FP8Q_EDEVICE, "no HIP device available");
+    }
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(FP8Q_ELAUNCH, "scratch address on device %d: %s", dev,
+                        e != hipSuccess ? hipGetErrorString(e) : "null address");
+        }
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return FP8Q_OK;
+}
+
 bool valid_hp(int hp) { return hp == FP8Q_F32 || hp == FP8Q_BF16; }
 bool valid_fmt(int f) { return f == FP8Q_E4M3 || f == FP8Q_E5M2; }
 bool valid_flags(unsigned f) { return (f & ~(FP8Q_SATURATE | FP8Q_COUNT_OVERFLOW)) == 0; }
@@ -375,9 +410,10 @@ static int check_quant_common(const void* x, int hp, int64_t rows, int64_t cols,
     return FP8Q_OK;
 }
 
-int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, int fmt, int scaling,
-                            fp8q_delayed_state* state, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
-                            unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of the per-tensor quantizer (its workspace aside).
+static int check_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, int fmt, int scaling,
+                            const fp8q_delayed_state* state, const uint8_t* q, const float* scale_out,
+                            unsigned flags) {
     int r;
     if ((r = check_quant_common(x, hp, rows, cols, fmt, q, flags, FP8Q_SATURATE | FP8Q_COUNT_OVERFLOW)) != FP8Q_OK)
         return r;
@@ -386,10 +422,15 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, i
     if (scaling == FP8Q_DELAYED && state == nullptr) return fail(FP8Q_EINVAL, "delayed scaling needs a state");
     if ((flags & FP8Q_COUNT_OVERFLOW) && scaling != FP8Q_DELAYED)
         return fail(FP8Q_EINVAL, "FP8Q_COUNT_OVERFLOW needs delayed scaling (the count lives in its state)");
-    if (ws == nullptr || ws_bytes < fp8q::kReduceWsBytes)
-        return fail(FP8Q_EWORKSPACE, "reduce workspace of %zu bytes needed", fp8q::kReduceWsBytes);
-    if ((r = check_device()) != FP8Q_OK) return r;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return FP8Q_OK;
+}
+
+// Enqueue the per-tensor quantizer with its reduce region at ws
+// (kReduceWsBytes, completion counters zero): the amax grid, then the cast.
+static int enqueue_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, int fmt, int scaling,
+                              fp8q_delayed_state* state, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
+                              unsigned flags, void* ws, hipStream_t s) {
+    int r;
     fp8q::QuantArgs a{};
     a.x = x; a.hp = hp; a.rows = rows; a.cols = cols; a.fmt = fmt;
     a.saturate = (flags & FP8Q_SATURATE) != 0;
@@ -409,6 +450,50 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, i
                       "amax")) != FP8Q_OK)
         return r;
     if ((r = launched(fp8q::launch_quantize(a, s), "quantize")) != FP8Q_OK) return r;
+    return FP8Q_OK;
+}
+
+int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols, int fmt, int scaling,
+                            fp8q_delayed_state* state, uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
+                            unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+    int r;
+    if ((r = check_per_tensor(x, hp, rows, cols, fmt, scaling, state, q, scale_out, flags)) != FP8Q_OK) return r;
+    if (ws == nullptr || ws_bytes < fp8q::kReduceWsBytes)
+        return fail(FP8Q_EWORKSPACE, "reduce workspace of %zu bytes needed", fp8q::kReduceWsBytes);
+    if ((r = check_device()) != FP8Q_OK) return r;
+    if ((r = enqueue_per_tensor(x, hp, rows, cols, fmt, scaling, state, q, qT, scale_out, amax_out, flags, ws,
+                                reinterpret_cast<hipStream_t>(stream))) != FP8Q_OK)
+        return r;
+    return ok();
+}
+
+int fp8_quantize_per_tensor_noalloc(const void* x, int hp, int64_t rows, int64_t cols, int fmt, int scaling,
+                                    fp8q_delayed_state* state, uint8_t* q, uint8_t* qT, float* scale_out,
+                                    float* amax_out, unsigned flags, void* stream) {
+    int r;
+    if ((r = check_per_tensor(x, hp, rows, cols, fmt, scaling, state, q, scale_out, flags)) != FP8Q_OK) return r;
+    // the reduce region's size does not depend on the input (the amax grid is
+    // capped at kReduceParts blocks), so every input size fits
+    if (fp8q::kReduceWsBytes > kScratchBytes)
+        return fail(FP8Q_EWORKSPACE, "the reduce region (%zu bytes) exceeds the library's %zu-byte scratch",
+                    fp8q::kReduceWsBytes, kScratchBytes);
+    if ((r = check_device()) != FP8Q_OK) return r;
+    void* ws = nullptr;
+    if ((r = scratch_address(&ws)) != FP8Q_OK) return r;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // The scratch keeps whatever the last call on this device left there.  Only
+    // delayed scaling's completion counters must start at zero (every call
+    // leaves them at zero, but a call that never ran to its end would not):
+    // clear them with a kernel, which a captured graph replays.
+    if (scaling == FP8Q_DELAYED &&
+        (r = launched(fp8q::launch_zero_words(reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) +
+                                                                          fp8q::kReduceCtrOffset),
+                                              (int64_t)(fp8q::kReduceCtrBytes / sizeof(uint32_t)), s),
+                      "clear")) != FP8Q_OK)
+        return r;
+    if ((r = enqueue_per_tensor(x, hp, rows, cols, fmt, scaling, state, q, qT, scale_out, amax_out, flags, ws, s)) !=
+        FP8Q_OK)
+        return r;
     return ok();
 }
 

@@ -70,6 +70,9 @@ hipError_t launch_amax_partials(const void* x, int hp, int64_t n, float* partial
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 
+// n 32-bit words at p set to zero by a kernel (capturable in a graph)
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t s);
+
 // codes [rows, cols] -> [cols, rows]
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out, hipStream_t s);
 

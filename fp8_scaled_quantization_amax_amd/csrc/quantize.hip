@@ -854,6 +854,19 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Zero n 32-bit words with plain vector stores: a kernel, not a memset, so
+// that it can sit inside a captured graph.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t s) {
+    const int64_t g = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(g < 1 ? 1 : g)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out, hipStream_t s) {
     const int64_t ntr = (rows + kTile - 1) / kTile, ntc = (cols + kTile - 1) / kTile;
     const int vin = ((uintptr_t)in % 16 == 0) && (cols % 16 == 0);

@@ -172,6 +172,26 @@ int fp8_quantize_per_tensor(const void* x, int hp, int64_t rows, int64_t cols,
                             unsigned flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp8_quantize_per_tensor without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments (minus ws,
+ * ws_bytes), same results, same errors.  Its reduce region lives in a 64 KiB
+ * array of device memory inside the library: each device holds one copy from
+ * its first call until the process ends, and the call allocates nothing (no
+ * hipMalloc, no allocating library routine).  The region's size does not
+ * depend on the input, so every size the workspace form takes fits; a build
+ * whose region outgrew the array would return FP8Q_EWORKSPACE.  All calls on
+ * one device share that array: calls that may overlap on a device (other
+ * streams, other host threads) race and must not be issued.  With DELAYED
+ * scaling each call first clears its completion counters with a kernel (no
+ * memset), so the call can be captured into a graph and replayed.
+ */
+int fp8_quantize_per_tensor_noalloc(const void* x, int hp, int64_t rows, int64_t cols,
+                                    int fmt, int scaling, fp8q_delayed_state* state,
+                                    uint8_t* q, uint8_t* qT, float* scale_out, float* amax_out,
+                                    unsigned flags, void* stream);
+
+/*
  * Per-tensor current scaling with a stochastically rounded cast (the
  * gradient rounding of "How to Optimize Transformer-Based Models for
  * Low-Precision Training", applied to the 8-bit formats).

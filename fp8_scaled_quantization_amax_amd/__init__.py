@@ -75,6 +75,7 @@ def lib():
             "fp8_gemm_scaled_NN": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
             "fp8_gemm_scaled_TN": (I, [I64, I64, I64, OP, OP, P, I, P, SZ, P]),
             "fp8q_mfma_loop": (I, [I, I, P, P]),
+            "fp8q_mfma_loop_data": (I, [I, I, I, P, P]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -156,12 +157,13 @@ class DelayedState:
 
 
 # ---------------------------------------------------------------- amax / quantize
-def fp8q_mfma_loop(blocks, iters, device="cuda"):
+def fp8q_mfma_loop(blocks, iters, device="cuda", random_operands=False):
     """Measurement aid (not the FP8 path): `blocks` x 256 threads, each wave
     running `iters` rounds of 8 register-only FP8 MFMAs; returns the per-thread
-    outputs (each exactly 4096 * iters for iters <= 4096)."""
+    outputs (each exactly 4096 * iters for iters <= 4096 with the default
+    all-ones operands; finite with random_operands, which needs iters % 8 == 0)."""
     out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
-    _check(lib().fp8q_mfma_loop(blocks, iters, _ptr(out), _stream()))
+    _check(lib().fp8q_mfma_loop_data(blocks, iters, 1 if random_operands else 0, _ptr(out), _stream()))
     return out
 
 

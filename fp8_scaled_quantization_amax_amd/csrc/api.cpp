@@ -543,15 +543,21 @@ int fp8_quantize_per_tensor_rht(const void* x, int hp, int64_t rows, int64_t col
     return ok();
 }
 
-int fp8q_mfma_loop(int blocks, int iters, float* out, void* stream) {
+int fp8q_mfma_loop_data(int blocks, int iters, int data, float* out, void* stream) {
     if (blocks <= 0 || iters <= 0 || out == nullptr)
         return fail(FP8Q_EINVAL, "blocks and iters must be positive and out non-NULL");
+    if (data != 0 && data != 1) return fail(FP8Q_EINVAL, "data must be 0 (ones) or 1 (random codes)");
+    if (data == 1 && iters % 8 != 0) return fail(FP8Q_EINVAL, "random-operand loop needs iters %% 8 == 0");
     int r;
     if ((r = check_device()) != FP8Q_OK) return r;
-    if ((r = launched(fp8q::launch_mfma_loop(blocks, iters, out, reinterpret_cast<hipStream_t>(stream)),
+    if ((r = launched(fp8q::launch_mfma_loop(blocks, iters, data, out, reinterpret_cast<hipStream_t>(stream)),
                       "mfma loop")) != FP8Q_OK)
         return r;
     return ok();
+}
+
+int fp8q_mfma_loop(int blocks, int iters, float* out, void* stream) {
+    return fp8q_mfma_loop_data(blocks, iters, 0, out, stream);
 }
 
 int fp8_quantize_tile1x128(const void* x, int hp, int64_t rows, int64_t cols, int axis, int fmt, uint8_t* q,

@@ -92,8 +92,10 @@ hipError_t launch_quantize_rht(const void* x, int hp, int64_t rows, int64_t cols
                                hipStream_t s);
 
 // Measurement aid: `blocks` workgroups of 256 threads, each wave running
-// `iters` rounds of 8 register-only FP8 MFMAs; out holds blocks * 256 floats.
-hipError_t launch_mfma_loop(int blocks, int iters, float* out, hipStream_t s);
+// `iters` rounds of 8 register-only FP8 MFMAs on all-ones operands (data 0)
+// or on pseudo-random codes that change every MFMA (data 1, iters % 8 == 0);
+// out holds blocks * 256 floats.
+hipError_t launch_mfma_loop(int blocks, int iters, int data, float* out, hipStream_t s);
 
 // Rowwise quantization: one fp32 scale per row (axis 0) or per column (axis
 // 1) into scales, codes into q [rows, cols], and (if qT != NULL) their

@@ -396,6 +396,17 @@ int fp8_gemm_scaled_TN(int64_t M, int64_t N, int64_t K, const fp8q_operand* A,
  */
 int fp8q_mfma_loop(int blocks, int iters, float* out, void* stream);
 
+/* fp8q_mfma_loop with a choice of operand data: data = 0 is fp8q_mfma_loop
+ * (all codes 1.0, exact output); data = 1 gives every lane 8 A and 8 B
+ * operand sets of pseudo-random E4M3 codes (random sign, normal exponent,
+ * any mantissa; never NaN) and feeds each MFMA a different pair, so the
+ * matrix cores see data that changes every instruction, as in a GEMM.  The
+ * cores' energy depends on their data, so under the chip's power limit this
+ * is the sustained rate for such data; its output is finite but not
+ * checkable exactly.  data = 1 needs iters % 8 == 0.  EINVAL otherwise, as
+ * fp8q_mfma_loop. */
+int fp8q_mfma_loop_data(int blocks, int iters, int data, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -166,6 +166,9 @@ def test_mfma_loop_validation():
     assert L.fp8q_mfma_loop(0, 16, fake, None) == fq.EINVAL
     assert L.fp8q_mfma_loop(4, 0, fake, None) == fq.EINVAL
     assert L.fp8q_mfma_loop(4, 16, None, None) == fq.EINVAL
+    assert L.fp8q_mfma_loop_data(4, 16, 2, fake, None) == fq.EINVAL      # unknown data
+    assert L.fp8q_mfma_loop_data(4, 12, 1, fake, None) == fq.EINVAL      # random needs iters % 8 == 0
+    assert L.fp8q_mfma_loop_data(0, 16, 1, fake, None) == fq.EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -119,6 +119,25 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
     return v > o ? v : o;
 }
 
+// Lane n (a compile-time constant after unrolling, 0..15) of each 16-lane
+// DPP row broadcast to the whole row (row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast_n(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_lane_bcast(float v, int n) {
+    switch (n) {
+        case 0: return row_bcast_n<0>(v);
+        case 1: return row_bcast_n<1>(v);
+        case 2: return row_bcast_n<2>(v);
+        case 3: return row_bcast_n<3>(v);
+        case 4: return row_bcast_n<4>(v);
+        case 5: return row_bcast_n<5>(v);
+        case 6: return row_bcast_n<6>(v);
+        default: return row_bcast_n<7>(v);
+    }
+}
+
 // Block-wide max of a per-thread key (blockDim.x == 256).  Uses 4 words of LDS.
 __device__ __forceinline__ uint32_t block_max_u32_256(uint32_t v, uint32_t* lds4) {
     v = wave_max_u32(v);

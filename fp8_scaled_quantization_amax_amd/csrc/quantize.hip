@@ -636,27 +636,55 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
 // maxima are reduced across 16 or 4 neighbouring lanes, and every lane stores
 // its 8 codes as one 8-byte word.  The flat unit index also gives the scale
 // index directly: unit u belongs to 1x128 tile u / 16 and MX block u / 4.
+// One loaded 8-element unit, kept as the raw 16 (bf16) or 32 (fp32) bytes
+// until it is cast, so that a thread's UNR units in flight cost 4 (8) VGPRs
+// each rather than 8 unpacked floats.
 template <int HP>
-__device__ __forceinline__ void load_unit(const void* __restrict__ x, int64_t u, float v[8]) {
-    if constexpr (HP == FP8Q_BF16) {
-        const uint4 w = load_stream16(reinterpret_cast<const uint4*>(x) + u);
-        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[2 * j] = __uint_as_float(d[j] << 16);
-            v[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+struct Unit {
+    uint4 w[HP == FP8Q_BF16 ? 1 : 2];
+
+    __device__ __forceinline__ void load(const void* __restrict__ x, int64_t u) {
+        if constexpr (HP == FP8Q_BF16) {
+            w[0] = load_stream16(reinterpret_cast<const uint4*>(x) + u);
+        } else {
+            w[0] = load_stream16(reinterpret_cast<const uint4*>(x) + 2 * u);
+            w[1] = load_stream16(reinterpret_cast<const uint4*>(x) + 2 * u + 1);
         }
-    } else {
-        const uint4 wa = load_stream16(reinterpret_cast<const uint4*>(x) + 2 * u);
-        const uint4 wb = load_stream16(reinterpret_cast<const uint4*>(x) + 2 * u + 1);
-        const float4 a = make_float4(__uint_as_float(wa.x), __uint_as_float(wa.y), __uint_as_float(wa.z),
-                                     __uint_as_float(wa.w));
-        const float4 b = make_float4(__uint_as_float(wb.x), __uint_as_float(wb.y), __uint_as_float(wb.z),
-                                     __uint_as_float(wb.w));
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
-}
+    // max |x| over the unit as an abs key (NaN sorts above Inf); bf16 keys
+    // are maximised two at a time as packed 16-bit integers
+    __device__ __forceinline__ uint32_t key() const {
+        if constexpr (HP == FP8Q_BF16) {
+            typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+            const uint32_t d[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+            us2 m = {0, 0};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[j] & 0x7fff7fffu));
+            const uint32_t a = m.x, b = m.y;
+            return (a > b ? a : b) << 16;
+        } else {
+            const uint32_t d[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+            uint32_t k = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { const uint32_t z = d[e] & 0x7fffffffu; k = k > z ? k : z; }
+            return k;
+        }
+    }
+    __device__ __forceinline__ void unpack(float v[8]) const {
+        if constexpr (HP == FP8Q_BF16) {
+            const uint32_t d[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = __uint_as_float(d[j] << 16);
+                v[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+            }
+        } else {
+            const uint32_t d[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(d[e]);
+        }
+    }
+};
 
 template <int HP, int FMT, int SCHEME, bool SAT>
 __global__ __launch_bounds__(256) void quantize_flat_kernel(QuantArgs a, int64_t nunits) {
@@ -690,47 +718,70 @@ __global__ __launch_bounds__(256) void quantize_flat_kernel(QuantArgs a, int64_t
     uint32_t key_all = 0;
     uint32_t nov = 0;   // overflowing elements (delayed scaling, COUNT_OVERFLOW)
     for (int64_t base = b0; base < b1; base += 256 * UNR) {
-        float v[UNR][8];
+        Unit<HP> raw[UNR];
         // units past the run's end re-read its last unit (loads stay
         // unconditional); nothing of theirs is stored or counted
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
             const int64_t u = base + k * 256 + t;
-            load_unit<HP>(a.x, u < b1 ? u : b1 - 1, v[k]);
+            raw[k].load(a.x, u < b1 ? u : b1 - 1);
+        }
+        // 1x128 tiles: the 16 lanes of a DPP row share a tile, so after the row
+        // reduction every lane of row g holds the maxima of the row's UNR tiles
+        // of this pass.  Rather than every lane working out the scale and
+        // reciprocal of its tile for every unit (two IEEE divisions per 8
+        // elements), lane k of each row works them out for unit k's tile, and
+        // a DPP row broadcast hands them to the rest of the row: one pair of
+        // divisions per lane per pass.
+        float tsc[UNR], trc[UNR];
+        if constexpr (SCHEME == kTileAxis0) {
+            const int c = t & 15;
+            uint32_t mine = 0;
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                const uint32_t key = row16_max_u32(raw[k].key());
+                if (k == c) mine = key;
+            }
+            const float sm = scale_from_amax<FMT>(__uint_as_float(mine));
+            const float rm = 1.0f / sm;
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                tsc[k] = row_lane_bcast(sm, k);
+                trc[k] = row_lane_bcast(rm, k);
+            }
         }
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
             const int64_t u = base + k * 256 + t;
             const bool valid = u < b1;
-            uint32_t key = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { const uint32_t z = abs_key(v[k][e]); key = key > z ? key : z; }
+            float v[8];
+            raw[k].unpack(v);
             float q[8];
             if constexpr (kPerTensor) {
-                if constexpr (SCHEME == kPerTensorDelayed) key_all = valid && key > key_all ? key : key_all;
+                if constexpr (SCHEME == kPerTensorDelayed) {
+                    const uint32_t key = raw[k].key();
+                    key_all = valid && key > key_all ? key : key_all;
+                }
                 float d[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    d[e] = div_by_scale(v[k][e], s_pt, r_pt);
+                    d[e] = div_by_scale(v[e], s_pt, r_pt);
                     q[e] = saturate<FMT, SAT>(d[e]);
                 }
                 if (SCHEME == kPerTensorDelayed && a.count_overflow && valid) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) nov += overflowed<FMT>(v[k][e], d[e]);
+                    for (int e = 0; e < 8; ++e) nov += overflowed<FMT>(v[e], d[e]);
                 }
             } else if constexpr (SCHEME == kTileAxis0) {
-                key = row16_max_u32(key);
-                const float sc = scale_from_amax<FMT>(__uint_as_float(key));
-                const float r = 1.0f / sc;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(div_by_scale(v[k][e], sc, r));
-                if (valid && (t & 15) == 0) a.scales[u >> 4] = sc;
+                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(div_by_scale(v[e], tsc[k], trc[k]));
+                if (valid && (t & 15) == 0) a.scales[u >> 4] = tsc[k];
             } else {   // kMxAxis0
-                key = quad_max_u32(key);
+                const uint32_t key = quad_max_u32(raw[k].key());
                 const int code = e8m0_from_scale(scale_from_amax<FMT>(__uint_as_float(key)));
                 const float inv = e8m0_recip(code);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(v[k][e] * inv);
+                for (int e = 0; e < 8; ++e) q[e] = saturate<FMT, SAT>(v[e] * inv);
                 if (valid && (t & 3) == 0) a.e8m0[u >> 2] = (uint8_t)code;
             }
             if (valid)

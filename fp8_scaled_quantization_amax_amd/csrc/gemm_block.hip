@@ -38,10 +38,14 @@ namespace fp8q {
 //  * The FMAs of fragment row i run under the MFMAs of row i + 1.  The last
 //    row's MFMAs (and the FMAs of the last two rows) run after the next
 //    barrier, from registers, while the next step's fragments are read.
-//  * What bounds it: per 1024 MFMA cycles of a K step a CU moves 96 KB of
-//    fragment reads and 48 KB of operand writes through LDS, and every
-//    MFMA is followed by four FMAs.  A 128 x 128 wave tile would halve the
-//    LDS traffic per MFMA but needs 256 accumulator VGPRs, all there are.
+//  * Where the time goes (counters): the MFMA pipes are busy about 0.4 of
+//    the cycles; the FMAs keep the VALU issuing about a third of the cycles,
+//    less than half of that under a running MFMA; the LDS is far from
+//    saturated (per 1024 MFMA cycles of a K step a CU moves 96 KB of
+//    fragment reads and 48 KB of operand writes through it).  A 128 x 128
+//    wave tile would halve the operand traffic per MFMA but needs 256
+//    accumulator VGPRs, all there are; eight waves of 64 x 64, or A
+//    fragments loaded straight into registers, measured slower.
 // bytes spanned by a fp32 scale array (rows >> rshift, ld, kstride) over nkb K blocks
 __device__ __forceinline__ int64_t scale_bytes(const GemmScale& s, int64_t rows, int64_t nkb) {
     return ((((rows - 1) >> s.rshift) * s.ld + (nkb - 1) * s.kstride) + 1) * 4;

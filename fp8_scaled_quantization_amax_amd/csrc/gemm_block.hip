@@ -55,6 +55,25 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, 0, 0));
 }
 
+// Fragment reads with immediate offsets.  For fragment rows starting at a
+// multiple of 16 the LDS chunk swizzle ((r / 2) % 8) depends on the lane's
+// row l % 16 only, so fragment row r0 + 16 i of a stage sits at a per-lane
+// offset fixed for the kernel (FragLane, for r0 = the wave's first row) plus
+// 16 i rows: one address register per stage and operand half, and every
+// read takes its row as the instruction's offset instead of an address add.
+struct FragLane {
+    uint32_t lo, hi;   // chunks g and g + 4 of row r0 + l % 16 (g = l / 16)
+};
+__device__ __forceinline__ FragLane frag_lane(int r0) {
+    const int l = threadIdx.x & 63, r = r0 + (l & 15), g = l >> 4;
+    return FragLane{(uint32_t)swz2(r, g), (uint32_t)swz2(r, g + 4)};
+}
+__device__ __forceinline__ v8i frag_at(const uint8_t* lo, const uint8_t* hi, int row16) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(lo + row16 * 16 * BK);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(hi + row16 * 16 * BK);
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
 template <int FA, int FB, int OUT, bool BROW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int ntm, int ntn) {
     constexpr int BNb = 128;
@@ -65,6 +84,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
     const int64_t M = g.M, N = g.N, K = g.K;
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
     const int wm = (w >> 1) * 128, wn = (w & 1) * 64;
+    const FragLane fa = frag_lane(wm), fb = frag_lane(wn);
     constexpr int kFmtA = FA == FP8Q_E4M3 ? 0 : 1;
     constexpr int kFmtB = FB == FP8Q_E4M3 ? 0 : 1;
     const int nt = ntm * ntn;
@@ -200,13 +220,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
             const uint8_t* lb = la + kTileBytes;
             uint8_t* dst = lds_all + ((par + kt + 2) % 3) * kStage;
             const uint8_t* gs = lds_sc + ((gi + gpar) & 1) * kScGroup + 4 * (kt & 3);
+            // per-lane fragment bases of this stage (rows wm + 16 i of A, wn + 16 j of B)
+            const uint8_t* alo = la + fa.lo;
+            const uint8_t* ahi = la + fa.hi;
+            const uint8_t* blo = lb + fb.lo;
+            const uint8_t* bhi = lb + fb.hi;
+            // scale rows of fragment row 0 / column fragment 0, read as integers: read
+            // as float, the compiler could not tell them from the direct-to-LDS
+            // loads in flight and waited for all of them
+            const uint8_t* gsa = gs + (wm + (l & 15)) * 16;
+            const uint8_t* gsb = gs + kScA + (wn + 4 * (l >> 4)) * 16;
+            // whole addresses in registers: the scale area's offset in LDS does not fit
+            // the reads' 16-bit offset field, which then would be added per read
+
             __builtin_amdgcn_sched_barrier(0);
-            a[0] = frag2(la, wm);
+            a[0] = frag_at(alo, ahi, 0);
             if constexpr (DEF) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     mfma_one(7, j);
-                    b[j] = frag2(lb, wn + 16 * j);
+                    b[j] = frag_at(blo, bhi, j);
 #pragma unroll
                     for (int u = 3 * j; u < 3 * j + 3; ++u) stage_load(ld, ko, dst, u);
                     fma_one(6, j);
@@ -214,11 +247,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = frag2(lb, wn + 16 * j);
+                for (int j = 0; j < 4; ++j) b[j] = frag_at(blo, bhi, j);
 #pragma unroll
                 for (int u = 0; u < 12; ++u) stage_load(ld, ko, dst, u);
             }
-            a[1] = frag2(la, wm + 16);
+            a[1] = frag_at(alo, ahi, 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -231,11 +264,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
             // instruction waits for these reads before it must
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                sraw[i] = *reinterpret_cast<const float*>(gs + (wm + 16 * i + (l & 15)) * 16);
+                sraw[i] = __uint_as_float(*reinterpret_cast<const uint32_t*>(gsa + 16 * i * 16));
             if constexpr (BROW) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
-                    sbr[q] = *reinterpret_cast<const float*>(gs + kScA + (wn + 16 * (q >> 2) + 4 * (l >> 4) + (q & 3)) * 16);
+                    sbr[q] = __uint_as_float(*reinterpret_cast<const uint32_t*>(gsb + (16 * (q >> 2) + (q & 3)) * 16));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -244,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                 for (int j = 0; j < 4; ++j) {
                     mfma_one(i, j);
                     if (j == 0) {
-                        a[(i + 1) & 1] = frag2(la, wm + 16 * (i + 1));
+                        a[(i + 1) & 1] = frag_at(alo, ahi, i + 1);
                         sf[i - 1] = BROW ? sraw[i - 1] : sraw[i - 1] * sbc;
                     }
                     fma_one(i - 1, j);

@@ -230,8 +230,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
             // loads in flight and waited for all of them
             const uint8_t* gsa = gs + (wm + (l & 15)) * 16;
             const uint8_t* gsb = gs + kScA + (wn + 4 * (l >> 4)) * 16;
-            // whole addresses in registers: the scale area's offset in LDS does not fit
-            // the reads' 16-bit offset field, which then would be added per read
 
             __builtin_amdgcn_sched_barrier(0);
             a[0] = frag_at(alo, ahi, 0);

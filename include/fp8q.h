@@ -52,7 +52,10 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 3
+/* Version 4: the GEMM workspace starts with its reduce region (so one
+ * zero-filled workspace serves calls of any shape), and the entry points
+ * fp8_quantize_per_tensor_noalloc and fp8q_mfma_loop_data were added. */
+#define FP8Q_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 typedef enum fp8q_status {

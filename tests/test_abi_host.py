@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fq.lib()
-    assert L.fp8q_abi_version() == 3
+    assert L.fp8q_abi_version() == 4
     assert L.fp8q_status_string(0) == b"ok"
     for s in range(1, 7):
         assert L.fp8q_status_string(s) not in (b"ok", b"unknown status")

@@ -45,7 +45,10 @@ namespace fp8q {
 //    fragment reads and 48 KB of operand writes through it).  A 128 x 128
 //    wave tile would halve the operand traffic per MFMA but needs 256
 //    accumulator VGPRs, all there are; eight waves of 64 x 64, or A
-//    fragments loaded straight into registers, measured slower.
+//    fragments loaded straight into registers, measured slower.  A stage's
+//    loads issued in one burst after the barrier queued behind each other
+//    and held the waves apart at every barrier (a timing copy without the
+//    barrier ran 9% faster); spread over the step they cost about 0.5%.
 // bytes spanned by a fp32 scale array (rows >> rshift, ld, kstride) over nkb K blocks
 __device__ __forceinline__ int64_t scale_bytes(const GemmScale& s, int64_t rows, int64_t nkb) {
     return ((((rows - 1) >> s.rshift) * s.ld + (nkb - 1) * s.kstride) + 1) * 4;
@@ -185,7 +188,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
         };
         // One K step.  Stage kt sits in buffer (par + kt) % 3; the step loads
         // stage kt + 2 (of this tile, or the next tile's stage kt + 2 - nk)
-        // into the buffer every wave finished with before the barrier.  With
+        // into the buffer every wave finished with before the barrier, two
+        // loads under each of fragment rows 1-6 (a tile's first step, with no
+        // rows of the previous step to run, issues them at once).  With
         // DEF the previous step's fragment row 7 is still open: its MFMAs run
         // first, straight after the barrier and from registers only, while
         // this step's fragments are read; its FMAs follow under row 0's MFMAs.
@@ -238,8 +243,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                 for (int j = 0; j < 4; ++j) {
                     mfma_one(7, j);
                     b[j] = frag_at(blo, bhi, j);
-#pragma unroll
-                    for (int u = 3 * j; u < 3 * j + 3; ++u) stage_load(ld, ko, dst, u);
                     fma_one(6, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -278,6 +281,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                         a[(i + 1) & 1] = frag_at(alo, ahi, i + 1);
                         sf[i - 1] = BROW ? sraw[i - 1] : sraw[i - 1] * sbc;
                     }
+                    // the next stages' loads, two per fragment row: issued all at
+                    // once after the barrier they queued behind each other and
+                    // held the waves apart at every barrier (+6.5%, wgrad +13-20%)
+                    if (DEF && (j & 1)) stage_load(ld, ko, dst, 2 * (i - 1) + (j >> 1));
                     fma_one(i - 1, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }

@@ -38,9 +38,9 @@ namespace fp8q {
 //  * The FMAs of fragment row i run under the MFMAs of row i + 1.  The last
 //    row's MFMAs (and the FMAs of the last two rows) run after the next
 //    barrier, from registers, while the next step's fragments are read.
-//  * Where the time goes (counters): the MFMA pipes are busy about 0.4 of
-//    the cycles; the FMAs keep the VALU issuing about a third of the cycles,
-//    less than half of that under a running MFMA; the LDS is far from
+//  * Where the time goes (counters): the MFMA pipes are busy 0.44 of the
+//    cycles (0.38 with row scales on both operands); the FMAs keep the VALU
+//    issuing 0.36 (0.47), half of that under a running MFMA; the LDS is far from
 //    saturated (per 1024 MFMA cycles of a K step a CU moves 96 KB of
 //    fragment reads and 48 KB of operand writes through it).  A 128 x 128
 //    wave tile would halve the operand traffic per MFMA but needs 256

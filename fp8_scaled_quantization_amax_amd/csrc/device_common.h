@@ -76,6 +76,19 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
     return (uint32_t)w;
 }
 
+// Two fp32 values -> two 8-bit codes in the low half of a dword (pack2_lo),
+// or into the high half of w (pack2_hi); the same conversions as pack4.
+template <int FMT>
+__device__ __forceinline__ uint32_t pack2_lo(float a, float b) {
+    if constexpr (FMT == FP8Q_E4M3) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    else return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t pack2_hi(float a, float b, uint32_t w) {
+    if constexpr (FMT == FP8Q_E4M3) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, true);
+    else return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)w, true);
+}
+
 // |x| as an ordered integer key: NaN patterns sort above +Inf, so an integer
 // max over keys is a NaN-propagating amax.
 __device__ __forceinline__ uint32_t abs_key(float v) { return __float_as_uint(v) & 0x7fffffffu; }
@@ -197,7 +210,9 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 // as 1, 2, 3", SC 2011): ten rounds of (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
 // with (hi0, lo0) = 0xD2511F53 * c0 and (hi1, lo1) = 0xCD9E8D57 * c2 as full
 // 64-bit products (one multiply-add instruction each); the key gains
-// 0x9E3779B9 and 0xBB67AE85 before each round after the first.
+// 0x9E3779B9 and 0xBB67AE85 before each round after the first.  Each
+// three-way XOR is one gfx950 three-input bitwise instruction (truth table
+// 0x96).
 __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                                uint32_t k1) {
 #pragma unroll
@@ -207,7 +222,8 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
             k1 += 0xBB67AE85u;
         }
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96),
+                       n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
         c0 = n0;
         c1 = (uint32_t)p1;
         c2 = n2;

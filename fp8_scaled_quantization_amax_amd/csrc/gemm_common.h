@@ -100,18 +100,4 @@ __device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rsrc, uint32_t vo
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-// Workgroups of the persistent kernel: one per CU, rounded down to a multiple
-// of the 8 XCDs (the kernel splits the tiles into 8 per-XCD ranges).
-inline int persistent_grid() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
-        cached[dev] = cus / 8 * 8;
-    }
-    return cached[dev];
-}
-
 }  // namespace fp8q

@@ -25,6 +25,21 @@ constexpr size_t kReduceCtrBytes = (1 + kReduceParts / kTicketGroup) * kTicketLi
 constexpr size_t kReduceWsBytes = kReduceCtrOffset + kReduceCtrBytes;
 static_assert(kReduceParts <= 256 * 8, "reduce_partials_256 folds at most 8 partials per thread");
 
+// Workgroups of a persistent kernel with one workgroup per CU: the CU count,
+// rounded down to a multiple of the 8 XCDs (the GEMMs split their tiles into
+// 8 per-XCD ranges).
+inline int persistent_grid() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        cached[dev] = cus / 8 * 8;
+    }
+    return cached[dev];
+}
+
 // Quantization schemes of the tiled quantize kernel.
 enum Scheme : int {
     kPerTensorCurrent = 0,  // s from the amax partials of a preceding amax grid

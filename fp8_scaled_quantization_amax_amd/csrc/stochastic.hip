@@ -28,8 +28,19 @@ namespace fp8q {
 // Stochastic rounding of a finite v to the format's grid with the word r (the
 // result is exactly a grid value, or the step past the largest one, which the
 // converter then overflows like any other value); NaN and Inf pass unchanged.
-// |v| = M 2^(e - 23) with the 24-bit significand M; the grid spacing is
-// 2^D with D = max(e, emin) - mantissa bits, so |v| / 2^D = M / 2^shift.
+// With D the grid spacing at |v| (2^(max(e, emin) - mantissa bits) for
+// |v| in [2^e, 2^(e + 1))), |v| = (n + f) D and the magnitude becomes
+// (n + 1) D when r + floor(f 2^32) >= 2^32, else n D.  Computed without
+// branches, in two ways selected at the end:
+//  * |v| >= 2^emin: D is the fp32 ulp of |v| times 2^(23 - mantissa bits), so
+//    f 2^32 is the fraction field's low 23 - mb bits shifted up by 9 + mb,
+//    whose low bits are zero; r then carries into bit 23 - mb of the
+//    magnitude's bits exactly when its own top 23 - mb bits do, so adding
+//    those to the bits and clearing the low ones rounds (a carry out of the
+//    fraction field moves to the next binade, which is the next grid value).
+//  * |v| < 2^emin: D = 2^(emin - mb) is fixed; y = |v| / D is exact (a power
+//    of two), n = floor(y), and (y - n) 2^32 is an exact float below 2^32
+//    whose conversion truncates to floor(f 2^32).
 // Where the round-to-nearest cast of v is finite (|v| <= 464 for E4M3, the
 // tie above 448 rounding down to it; |v| < 61440 for E5M2) the result is
 // capped at fmax: current scaling leaves the amax element an ulp or two above
@@ -38,28 +49,22 @@ template <int FMT>
 __device__ __forceinline__ float sr_round(float v, uint32_t r) {
     constexpr int MB = FMT == FP8Q_E4M3 ? 3 : 2;
     constexpr int EMIN = FMT == FP8Q_E4M3 ? -6 : -14;
+    constexpr uint32_t kLow = (1u << (23 - MB)) - 1u;
+    constexpr uint32_t kMinNormal = (uint32_t)(EMIN + 127) << 23;                  // 2^emin
+    constexpr float kToGrid = (float)(1u << (MB - EMIN));                           // 1 / D below 2^emin
+    constexpr float kFromGrid = 1.0f / kToGrid;
+    constexpr uint32_t kRneFiniteBits = FMT == FP8Q_E4M3 ? 0x43e80000u : 0x476fffffu;  // 464, below 61440
     const uint32_t ab = __float_as_uint(v) & 0x7fffffffu;
-    if (ab >= 0x7f800000u) return v;
-    const bool normal = ab >= 0x00800000u;
-    const uint32_t M = (ab & 0x7fffffu) | (normal ? 0x800000u : 0u);
-    const int e = normal ? (int)(ab >> 23) - 127 : -126;
-    const int D = (e > EMIN ? e : EMIN) - MB;
-    const int shift = D - (e - 23);   // at least 23 - MB
-    uint32_t n = 0, frac32 = 0;       // |v| / 2^D = n + frac32 / 2^32 (+ less than 2^-32)
-    if (shift < 24) {
-        n = M >> shift;
-        frac32 = (M & ((1u << shift) - 1u)) << (32 - shift);
-    } else if (shift <= 32) {
-        frac32 = M << (32 - shift);
-    } else if (shift < 56) {
-        frac32 = M >> (shift - 32);
-    }
-    const uint32_t up = r > 0xffffffffu - frac32 ? 1u : 0u;   // r + frac32 >= 2^32
-    float mag = (float)(n + up) * __uint_as_float((uint32_t)(D + 127) << 23);
-    const float av = __uint_as_float(ab);
-    const bool rne_finite = FMT == FP8Q_E4M3 ? av <= 464.0f : av < 61440.0f;
-    if (rne_finite && mag > fmt_max<FMT>()) mag = fmt_max<FMT>();
-    return __builtin_copysignf(mag, v);
+    const uint32_t big = (ab + (r >> (9 + MB))) & ~kLow;
+    const float y = __uint_as_float(ab) * kToGrid;
+    const float n = __builtin_floorf(y);
+    const uint32_t frac32 = (uint32_t)((y - n) * 4294967296.0f);
+    const float small = (r > ~frac32 ? n + 1.0f : n) * kFromGrid;
+    // the cap compares bit patterns: for non-negative floats their order as
+    // unsigned integers is the order of the values
+    const uint32_t mag = ab < kMinNormal ? __float_as_uint(small) : big;
+    const uint32_t capped = __builtin_elementwise_min(mag, ab <= kRneFiniteBits ? __float_as_uint(fmt_max<FMT>()) : 0xffffffffu);
+    return ab >= 0x7f800000u ? v : __uint_as_float(capped | (__float_as_uint(v) & 0x80000000u));
 }
 
 template <int HP>
@@ -68,8 +73,9 @@ __device__ __forceinline__ float load_one_sr(const void* __restrict__ x, int64_t
     else return reinterpret_cast<const float*>(x)[i];
 }
 
-// VEC: n % 4 == 0 is not needed (the tail group is scalar), but x must be
-// aligned to 4 elements and q to 4 bytes.
+// VEC: x aligned to 4 elements and q to 4 bytes.  The grid strides over the
+// n / 4 whole groups without per-element checks; the last thread of block 0
+// casts the partial group at the end, if any.
 template <int HP, int FMT, bool SAT, bool VEC>
 __global__ __launch_bounds__(256) void quantize_sr_kernel(const void* __restrict__ x, int64_t n,
                                                           const float* __restrict__ partials, int nparts,
@@ -80,40 +86,48 @@ __global__ __launch_bounds__(256) void quantize_sr_kernel(const void* __restrict
     const float amax = reduce_partials_256(partials, nparts, red);
     const float s = scale_from_amax<FMT>(amax);
     const float rc = 1.0f / s;
-    const int64_t ngroups = (n + 3) / 4;
-    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < ngroups; g += (int64_t)gridDim.x * 256) {
+    auto cast4 = [&](int64_t g, const float (&v)[4]) {
         const uint4 rw = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), o0, o1, k0, k1);
-        const uint32_t rr[4] = {rw.x, rw.y, rw.z, rw.w};
+        return pack4<FMT>(saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[0], s, rc), rw.x)),
+                          saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[1], s, rc), rw.y)),
+                          saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[2], s, rc), rw.z)),
+                          saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[3], s, rc), rw.w)));
+    };
+    const int64_t nfull = n / 4;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < nfull; g += (int64_t)gridDim.x * 256) {
         const int64_t i0 = 4 * g;
-        const bool full = i0 + 4 <= n;
         float v[4];
-        if (VEC && full) {
-            if constexpr (HP == FP8Q_BF16) {
-                const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + i0);
-                v[0] = __uint_as_float(w.x << 16);
-                v[1] = __uint_as_float(w.x & 0xffff0000u);
-                v[2] = __uint_as_float(w.y << 16);
-                v[3] = __uint_as_float(w.y & 0xffff0000u);
-            } else {
-                const uint4 w = load_stream16(reinterpret_cast<const float*>(x) + i0);
-                v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
-                v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
-            }
+        if constexpr (VEC && HP == FP8Q_BF16) {
+            const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + i0);
+            v[0] = __uint_as_float(w.x << 16);
+            v[1] = __uint_as_float(w.x & 0xffff0000u);
+            v[2] = __uint_as_float(w.y << 16);
+            v[3] = __uint_as_float(w.y & 0xffff0000u);
+        } else if constexpr (VEC) {
+            const uint4 w = load_stream16(reinterpret_cast<const float*>(x) + i0);
+            v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+            v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = i0 + e < n ? load_one_sr<HP>(x, i0 + e) : 0.0f;
+            for (int e = 0; e < 4; ++e) v[e] = load_one_sr<HP>(x, i0 + e);
         }
-        float c[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c[e] = saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[e], s, rc), rr[e]));
-        const uint32_t w = pack4<FMT>(c[0], c[1], c[2], c[3]);
-        if (VEC && full) {
+        const uint32_t w = cast4(g, v);
+        if constexpr (VEC) {
             *reinterpret_cast<uint32_t*>(q + i0) = w;
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (i0 + e < n) q[i0 + e] = (uint8_t)((w >> (8 * e)) & 0xffu);
+            for (int e = 0; e < 4; ++e) q[i0 + e] = (uint8_t)((w >> (8 * e)) & 0xffu);
         }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 255 && (n & 3)) {
+        const int64_t i0 = 4 * nfull;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = i0 + e < n ? load_one_sr<HP>(x, i0 + e) : 0.0f;
+        const uint32_t w = cast4(nfull, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (i0 + e < n) q[i0 + e] = (uint8_t)((w >> (8 * e)) & 0xffu);
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         *scale_out = s;

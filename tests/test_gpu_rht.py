@@ -35,6 +35,22 @@ def test_rht_bit_exact(shape, dtype, fmt):
     check_rht(x, fmt, seed=0xFEEDFACE12345678)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt", [fq.E5M2, fq.E4M3], ids=["e5m2", "e4m3"])
+@pytest.mark.parametrize("outlier", [1.0, None], ids=["with_outlier", "all_tiny"])
+def test_rht_tiny_values(dtype, fmt, outlier):
+    """Subnormal inputs, so that H16 (d x) falls below 2^-124 and a quarter of it
+    is inexact: with a normal outlier setting the scale (tiny quotients, zero
+    codes of either sign) and with every value tiny (the amax itself a rounded
+    quarter, the scale at its 1e-12 floor).  Codes, scale and amax bit-exact."""
+    announce("rht tiny", dtype, fmt, outlier)
+    x = workloads.normal((64, 520), 1e-39, 9800, dtype)
+    assert (x != 0).float().mean() > 0.5 and x.abs().max() < 1e-37
+    if outlier is not None:
+        x[17, 300] = outlier
+    check_rht(x, fmt, seed=0x5EED)
+
+
 def test_rht_full_size_gradient():
     """bf16 [15872, 4096] ~ N(0,1) with a few outliers, E5M2, with the K-major copy."""
     announce("rht full size")

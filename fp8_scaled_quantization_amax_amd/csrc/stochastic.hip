@@ -25,48 +25,6 @@
 
 namespace fp8q {
 
-// Stochastic rounding of a finite v to the format's grid with the word r (the
-// result is exactly a grid value, or the step past the largest one, which the
-// converter then overflows like any other value); NaN and Inf pass unchanged.
-// With D the grid spacing at |v| (2^(max(e, emin) - mantissa bits) for
-// |v| in [2^e, 2^(e + 1))), |v| = (n + f) D and the magnitude becomes
-// (n + 1) D when r + floor(f 2^32) >= 2^32, else n D.  Computed without
-// branches, in two ways selected at the end:
-//  * |v| >= 2^emin: D is the fp32 ulp of |v| times 2^(23 - mantissa bits), so
-//    f 2^32 is the fraction field's low 23 - mb bits shifted up by 9 + mb,
-//    whose low bits are zero; r then carries into bit 23 - mb of the
-//    magnitude's bits exactly when its own top 23 - mb bits do, so adding
-//    those to the bits and clearing the low ones rounds (a carry out of the
-//    fraction field moves to the next binade, which is the next grid value).
-//  * |v| < 2^emin: D = 2^(emin - mb) is fixed; y = |v| / D is exact (a power
-//    of two), n = floor(y), and (y - n) 2^32 is an exact float below 2^32
-//    whose conversion truncates to floor(f 2^32).
-// Where the round-to-nearest cast of v is finite (|v| <= 464 for E4M3, the
-// tie above 448 rounding down to it; |v| < 61440 for E5M2) the result is
-// capped at fmax: current scaling leaves the amax element an ulp or two above
-// fmax, and rounding it up to the next step would overflow.
-template <int FMT>
-__device__ __forceinline__ float sr_round(float v, uint32_t r) {
-    constexpr int MB = FMT == FP8Q_E4M3 ? 3 : 2;
-    constexpr int EMIN = FMT == FP8Q_E4M3 ? -6 : -14;
-    constexpr uint32_t kLow = (1u << (23 - MB)) - 1u;
-    constexpr uint32_t kMinNormal = (uint32_t)(EMIN + 127) << 23;                  // 2^emin
-    constexpr float kToGrid = (float)(1u << (MB - EMIN));                           // 1 / D below 2^emin
-    constexpr float kFromGrid = 1.0f / kToGrid;
-    constexpr uint32_t kRneFiniteBits = FMT == FP8Q_E4M3 ? 0x43e80000u : 0x476fffffu;  // 464, below 61440
-    const uint32_t ab = __float_as_uint(v) & 0x7fffffffu;
-    const uint32_t big = (ab + (r >> (9 + MB))) & ~kLow;
-    const float y = __uint_as_float(ab) * kToGrid;
-    const float n = __builtin_floorf(y);
-    const uint32_t frac32 = (uint32_t)((y - n) * 4294967296.0f);
-    const float small = (r > ~frac32 ? n + 1.0f : n) * kFromGrid;
-    // the cap compares bit patterns: for non-negative floats their order as
-    // unsigned integers is the order of the values
-    const uint32_t mag = ab < kMinNormal ? __float_as_uint(small) : big;
-    const uint32_t capped = __builtin_elementwise_min(mag, ab <= kRneFiniteBits ? __float_as_uint(fmt_max<FMT>()) : 0xffffffffu);
-    return ab >= 0x7f800000u ? v : __uint_as_float(capped | (__float_as_uint(v) & 0x80000000u));
-}
-
 template <int HP>
 __device__ __forceinline__ float load_one_sr(const void* __restrict__ x, int64_t i) {
     if constexpr (HP == FP8Q_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[i]);

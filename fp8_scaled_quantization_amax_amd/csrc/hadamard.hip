@@ -236,23 +236,30 @@ __global__ __launch_bounds__(256, 2) void rht_cast_kernel(const void* __restrict
     auto unit = [&](const UnitRows<HP>& cur, int64_t u) {
         const int64_t b = u / ncg, c0 = (u % ncg) * 8;
         const uint32_t signs = unit_signs(b, k0, k1);
-        // codes of columns 4 h .. 4 h + 3, stored as one dword per row
+        // bf16: the 8 codes of a row in one store (two 4-byte halves stored
+        // apart cost 1.5x the write traffic: partial lines).  fp32, whose rows
+        // take twice the registers, stores the halves apart.
+        constexpr int kParts = HP == FP8Q_BF16 ? 1 : 2, kPairs = 4 / kParts;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t w[16];
+        for (int h = 0; h < kParts; ++h) {
+            uint32_t w[16][2];
 #pragma unroll
-            for (int j = 2 * h; j < 2 * h + 2; ++j) {
+            for (int jj = 0; jj < kPairs; ++jj) {
                 float za[16], zb[16];
-                unit_pair<HP>(cur, j, signs, za, zb);
+                unit_pair<HP>(cur, h * kPairs + jj, signs, za, zb);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float ca = saturate<FMT, SAT>(div_by_scale(za[i], s4, rc4));
                     const float cb = saturate<FMT, SAT>(div_by_scale(zb[i], s4, rc4));
-                    w[i] = (j & 1) ? pack2_hi<FMT>(ca, cb, w[i]) : pack2_lo<FMT>(ca, cb);
+                    w[i][jj >> 1] = (jj & 1) ? pack2_hi<FMT>(ca, cb, w[i][jj >> 1]) : pack2_lo<FMT>(ca, cb);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(q + (b * 16 + i) * cols + c0 + 4 * h) = w[i];
+            for (int i = 0; i < 16; ++i) {
+                uint8_t* dst = q + (b * 16 + i) * cols + c0;
+                if constexpr (kParts == 1) *reinterpret_cast<uint2*>(dst) = make_uint2(w[i][0], w[i][1]);
+                else *reinterpret_cast<uint32_t*>(dst + 4 * h) = w[i][0];
+            }
         }
     };
     run_units<HP>(x, cols, ncg, nunits, stride, stage, unit);

@@ -93,6 +93,20 @@ __host__ __device__ __forceinline__ float sr_round(float v, uint32_t r) {
     return ab >= 0x7f800000u ? v : __builtin_bit_cast(float, capped | (__builtin_bit_cast(uint32_t, v) & 0x80000000u));
 }
 
+// div_by_scale for a finite scale s = max(amax / fmax, 1e-12) formed from
+// the amax of the very tensor x belongs to: then |x| <= amax, so |x / s| stays
+// within an ulp of fmax, the quotient estimate x r is finite and the check for
+// a non-finite one is dead; the two residual steps are the same.  (A
+// non-finite s comes from an infinite or NaN amax; div_by_scale returns x r
+// for it, which callers take on a separate, uniform path.)
+__host__ __device__ __forceinline__ float div_by_own_scale(float x, float s, float r) {
+    const float q0 = x * r;
+    float e = __builtin_fmaf(-q0, s, x);
+    const float q1 = __builtin_fmaf(e, r, q0);
+    e = __builtin_fmaf(-q1, s, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, q1), x);
+}
+
 // Optional saturation: |v| > fmax -> +-fmax (NaN unchanged).
 template <int FMT, bool SAT>
 __device__ __forceinline__ float saturate(float v) {

@@ -46,6 +46,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -233,9 +235,15 @@ __global__ __launch_bounds__(256, 2) void rht_cast_kernel(const void* __restrict
     const float s = scale_from_amax<FMT>(amax);
     const float s4 = 4.0f * s, rc4 = 0.25f * (1.0f / s);   // 4 s and RN(1 / (4 s)), both exact scalings
     const int64_t ncg = cols / 8, nunits = rows / 16 * ncg, stride = (int64_t)gridDim.x * 256;
+    // a finite s comes from this tensor's own amax, so the division needs no
+    // check for a non-finite quotient; an infinite or NaN s gives z * (1 / 4s)
+    // for every element (separate copies of the loop)
+    auto run = [&](auto finite_c) {
+    constexpr bool FIN = decltype(finite_c)::value;
     auto unit = [&](const UnitRows<HP>& cur, int64_t u) {
         const int64_t b = u / ncg, c0 = (u % ncg) * 8;
         const uint32_t signs = unit_signs(b, k0, k1);
+        auto div = [&](float z) { return FIN ? div_by_own_scale(z, s4, rc4) : z * rc4; };
         // bf16: the 8 codes of a row in one store (two 4-byte halves stored
         // apart cost 1.5x the write traffic: partial lines).  fp32, whose rows
         // take twice the registers, stores the halves apart.
@@ -249,8 +257,8 @@ __global__ __launch_bounds__(256, 2) void rht_cast_kernel(const void* __restrict
                 unit_pair<HP>(cur, h * kPairs + jj, signs, za, zb);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float ca = saturate<FMT, SAT>(div_by_scale(za[i], s4, rc4));
-                    const float cb = saturate<FMT, SAT>(div_by_scale(zb[i], s4, rc4));
+                    const float ca = saturate<FMT, SAT>(div(za[i]));
+                    const float cb = saturate<FMT, SAT>(div(zb[i]));
                     w[i][jj >> 1] = (jj & 1) ? pack2_hi<FMT>(ca, cb, w[i][jj >> 1]) : pack2_lo<FMT>(ca, cb);
                 }
             }
@@ -263,6 +271,9 @@ __global__ __launch_bounds__(256, 2) void rht_cast_kernel(const void* __restrict
         }
     };
     run_units<HP>(x, cols, ncg, nunits, stride, stage, unit);
+    };
+    if (__builtin_isfinite(s)) run(std::true_type{});
+    else run(std::false_type{});
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         *scale_out = s;
         if (amax_out) *amax_out = amax;

@@ -20,6 +20,8 @@
 // traffic of the group, so the kernel is ALU-bound.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -44,12 +46,19 @@ __global__ __launch_bounds__(256) void quantize_sr_kernel(const void* __restrict
     const float amax = reduce_partials_256(partials, nparts, red);
     const float s = scale_from_amax<FMT>(amax);
     const float rc = 1.0f / s;
+    // A finite s comes from this tensor's own amax, so the division needs no
+    // check for a non-finite quotient; an infinite or NaN s (an infinite or
+    // NaN amax) gives x / s = x * (1 / s) for every element.  The two cases
+    // run as separate copies of the loop.
+    auto run = [&](auto finite_c) {
+    constexpr bool FIN = decltype(finite_c)::value;
     auto cast4 = [&](int64_t g, const float (&v)[4]) {
         const uint4 rw = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), o0, o1, k0, k1);
-        return pack4<FMT>(saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[0], s, rc), rw.x)),
-                          saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[1], s, rc), rw.y)),
-                          saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[2], s, rc), rw.z)),
-                          saturate<FMT, SAT>(sr_round<FMT>(div_by_scale(v[3], s, rc), rw.w)));
+        auto div = [&](float xv) { return FIN ? div_by_own_scale(xv, s, rc) : xv * rc; };
+        return pack4<FMT>(saturate<FMT, SAT>(sr_round<FMT>(div(v[0]), rw.x)),
+                          saturate<FMT, SAT>(sr_round<FMT>(div(v[1]), rw.y)),
+                          saturate<FMT, SAT>(sr_round<FMT>(div(v[2]), rw.z)),
+                          saturate<FMT, SAT>(sr_round<FMT>(div(v[3]), rw.w)));
     };
     const int64_t nfull = n / 4;
     for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < nfull; g += (int64_t)gridDim.x * 256) {
@@ -87,6 +96,9 @@ __global__ __launch_bounds__(256) void quantize_sr_kernel(const void* __restrict
         for (int e = 0; e < 4; ++e)
             if (i0 + e < n) q[i0 + e] = (uint8_t)((w >> (8 * e)) & 0xffu);
     }
+    };
+    if (__builtin_isfinite(s)) run(std::true_type{});
+    else run(std::false_type{});
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         *scale_out = s;
         if (amax_out) *amax_out = amax;

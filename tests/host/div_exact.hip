@@ -1,7 +1,9 @@
 // Host-side check of the quantizers' division: fp8q::div_by_scale(x, s, 1/s)
 // must equal the correctly rounded fp32 quotient RN32(x / s) wherever the
 // quotient can influence an 8-bit code (2^-18 <= |x/s| < 2^17); outside that
-// range every candidate encodes to the same code (zero, or overflow).
+// range every candidate encodes to the same code (zero, or overflow).  And
+// fp8q::div_by_own_scale must give div_by_scale's bits wherever x / s's
+// estimate x (1/s) is finite.
 // Compiled as host code from the kernels' own header.
 #include <cmath>
 #include <cstdint>
@@ -29,6 +31,13 @@ static inline int relevant_mismatch(float x, float s, float r) {
     return 1;
 }
 
+// div_by_own_scale drops div_by_scale's check for a non-finite estimate x r,
+// which its callers rule out: the same bits wherever x r is finite
+static inline int own_mismatch(float x, float s, float r) {
+    if (!(std::fabs(x * r) <= 3.402823466e38f)) return 0;
+    return b_of(fp8q::div_by_own_scale(x, s, r)) == b_of(fp8q::div_by_scale(x, s, r)) ? 0 : 1;
+}
+
 int main(int argc, char** argv) {
     const int nscales = argc > 1 ? std::atoi(argv[1]) : 20000;
     std::vector<float> scales = {1e-12f, 1.0f, 448.0f / 448.0f, 1.0f / 448.0f, 1.0f / 57344.0f, 1.0f / 3.0f,
@@ -44,7 +53,7 @@ int main(int argc, char** argv) {
 #pragma omp parallel for reduction(+ : bad) schedule(dynamic, 64)
     for (int si = 0; si < (int)scales.size(); ++si) {
         const float s = scales[si], r = 1.0f / s;
-        for (uint32_t b = 0; b < 65536; ++b) bad += relevant_mismatch(f_of(b << 16), s, r);
+        for (uint32_t b = 0; b < 65536; ++b) bad += relevant_mismatch(f_of(b << 16), s, r) + own_mismatch(f_of(b << 16), s, r);
     }
     std::printf("bf16 x %zu scales: %ld relevant mismatches\n", scales.size(), bad);
     // every fp32 input against a few scales
@@ -55,7 +64,8 @@ int main(int argc, char** argv) {
         const float s = full[fi];
         const float r = 1.0f / s;
 #pragma omp parallel for reduction(+ : bad2) schedule(static)
-        for (long long i = 0; i < (1LL << 32); ++i) bad2 += relevant_mismatch(f_of((uint32_t)i), s, r);
+        for (long long i = 0; i < (1LL << 32); ++i)
+            bad2 += relevant_mismatch(f_of((uint32_t)i), s, r) + own_mismatch(f_of((uint32_t)i), s, r);
     }
     std::printf("all fp32 x %d scales: %ld relevant mismatches\n", nfull, bad2);
     // an infinite scale (an infinite amax): x / Inf exactly, sign of zero included

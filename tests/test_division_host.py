@@ -1,6 +1,7 @@
 """The quantizers divide by the scale with a reciprocal and two FMA residual
 corrections instead of a full IEEE division.  This CPU test compiles that very
-helper (csrc/device_common.h, div_by_scale) as host code and checks it against
+helper (csrc/device_common.h, div_by_scale, and div_by_own_scale where its
+caller guarantees a finite estimate) as host code and checks it against
 the correctly rounded fp32 quotient: every bf16 input against 2000 scales,
 every fp32 input against one scale, and every bf16 input against an infinite
 scale (x / Inf: +-0 for finite x, NaN otherwise)."""

@@ -84,3 +84,27 @@ def test_sr_amax_element_stays_finite(fmt):
     x = x.to(torch.bfloat16).reshape(16, 256)
     q = check_sr(x, fmt, seed, off)
     assert int(q[0, 0].item()) == (0x7E if fmt == fq.E4M3 else 0x7B)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt", [fq.E5M2, fq.E4M3], ids=["e5m2", "e4m3"])
+def test_sr_outliers_misaligned(dtype, fmt):
+    """Outliers x1e4 put most quotients below the format's smallest normal,
+    where the rounding takes its below-2^emin path in nearly every wave; the
+    input starts one element past an aligned address (no vector loads), and
+    the element count leaves a partial group of four."""
+    announce("sr outliers misaligned", dtype, fmt)
+    rows, cols = 300, 257
+    flat = workloads.normal((rows * cols + 1,), 1.0, 9400, dtype)
+    big = 1e4 if fmt == fq.E4M3 else 1e9   # E5M2's normal range reaches 2^-14 * fmax below the amax
+    flat[1 + torch.randperm(rows * cols, generator=torch.Generator().manual_seed(9401))[:40]] *= big
+    x = flat[1:].view(rows, cols)
+    xd = flat.to(dev())[1:].view(rows, cols)
+    assert xd.data_ptr() % 8 != 0
+    q, _, s, a = fq.fp8_quantize_per_tensor_sr(xd, fmt, 0xABCDEF, 3)
+    torch.cuda.synchronize()
+    oq, os_, oa = oracle.quantize_per_tensor_sr(host_input(x), fmt, 0xABCDEF, 3, False)
+    assert s.item() == os_ and a.item() == oa
+    assert codes_equal(q.cpu().numpy(), oq.reshape(q.shape), fmt)
+    small = (q.cpu().numpy() & 0x7F) < (0x08 if fmt == fq.E4M3 else 0x04)   # below the smallest normal code
+    assert small.mean() > 0.5

@@ -384,11 +384,11 @@ int fp8_amax(const void* x, int hp, int64_t n, float* amax_out, void* ws, size_t
     if ((r = check_device()) != FP8Q_OK) return r;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* partials = reinterpret_cast<float*>(ws);
-    // the folded form's completion chain grows with the block count: 512
-    // blocks (two per CU) keep the stream at full rate and the tail short
-    // (bf16 [15872, 4096]: 22.5-23.0 us against 23.1-23.6 with 1024 and
-    // 24.6-25.8 with 256 or 2048)
-    const int np = std::min(fp8q::amax_partials_grid(n), 512);
+    // the folded form's completion chain grows with the block count: the
+    // grid's 512 blocks (two per CU) keep the stream at full rate and the
+    // tail short (bf16 [15872, 4096]: 22.5-23.0 us against 23.1-23.6 with
+    // 1024 and 24.6-25.8 with 256 or 2048)
+    const int np = fp8q::amax_partials_grid(n);
     uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
     uint32_t* keys = reinterpret_cast<uint32_t*>(wsb + fp8q::kReduceKeysOffset);
     uint32_t* ctrs = reinterpret_cast<uint32_t*>(wsb + fp8q::kReduceCtrOffset);

@@ -157,11 +157,15 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const void* __restri
     if (threadIdx.x == 0) *amax_out = __uint_as_float(all);
 }
 
+// At most 512 blocks (two per CU): every block of the cast that follows folds
+// these partials again, and 512 of them instead of 2048 made the transposing
+// per-tensor cast 5% and the SR cast 4% faster on bf16 [15872, 4096] (the
+// flat cast 1% slower, the autocast layer 0.4% faster; A/B in one call).
 int amax_partials_grid(int64_t n) {
     const int64_t per_block = 256 * 8 * 8;   // 8 vectors of up to 8 elements per thread
     int64_t g = (n + per_block - 1) / per_block;
     if (g < 1) g = 1;
-    if (g > kReduceParts) g = kReduceParts;
+    if (g > 512) g = 512;
     return (int)g;
 }
 

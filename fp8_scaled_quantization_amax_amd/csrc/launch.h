@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp8q.h"
 
 namespace fp8q {
@@ -28,16 +30,19 @@ static_assert(kReduceParts <= 256 * 8, "reduce_partials_256 folds at most 8 part
 // Workgroups of a persistent kernel with one workgroup per CU: the CU count,
 // rounded down to a multiple of the 8 XCDs (the GEMMs split their tiles into
 // 8 per-XCD ranges).
+// (Cached per device; threads that race to fill an entry store the same value.)
 inline int persistent_grid() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
+    int g = cached[dev].load(std::memory_order_relaxed);
+    if (g == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
-        cached[dev] = cus / 8 * 8;
+        g = cus / 8 * 8;
+        cached[dev].store(g, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return g;
 }
 
 // Quantization schemes of the tiled quantize kernel.

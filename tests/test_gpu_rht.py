@@ -25,10 +25,14 @@ def check_rht(x, fmt, seed, emit_t=True):
     return q, qT, s, oq, os_
 
 
-@pytest.mark.parametrize("shape", [(16, 8), (32, 24), (256, 4096), (1024, 520)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("shape", [(16, 8), (32, 24), (16, 64), (48, 512), (256, 4096), (1024, 520)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("fmt", [fq.E5M2, fq.E4M3], ids=["e5m2", "e4m3"])
 def test_rht_bit_exact(shape, dtype, fmt):
+    """16x64: one partial wave of 8 units in one 16-row block (the wave-shared
+    signs with lanes 8-63 idle); 48x512: every wave inside one block; 32x24 and
+    1024x520: waves spanning blocks (per-lane signs)."""
     announce("rht", shape, dtype, fmt)
     x = workloads.normal(shape, 1.0, 9500 + shape[0] + shape[1], dtype)
     x[shape[0] // 3, shape[1] // 2] = 500.0   # an outlier to spread

@@ -515,21 +515,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
         const uint8_t* la = lds_ab[(kt + par) & 1];
         const uint8_t* lb = la + kTileBytes;
         if constexpr (MX) {
-            if constexpr (DEFERRED) {
-                // the previous step read this step's scale bytes
-#pragma unroll
-                for (int i = 0; i < 2; ++i) sa_o[i] = sa[6 + i];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sb_o[j] = sb[j];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) sa[i] = sa_n[i];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sb[j] = sb_n[j];
-            } else {
-                // a tile's first step reads its own, before every fragment
-                // read so that the waits below cover them too
-                read_scales(kt, sa, sb);
-            }
+            // a tile's first step reads its own scale bytes, before every
+            // fragment read so that the waits below cover them too (later
+            // steps' were read, and moved into place, by the previous step)
+            if constexpr (!DEFERRED) read_scales(kt, sa, sb);
             __builtin_amdgcn_sched_barrier(0);
         }
         // previous step's rows 6, 7 (column-major, registers only) while
@@ -583,6 +572,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int nt
             if (m < 4) rdh(ay[m >> 1], la, wm + 96 + 16 * (m >> 1), m & 1);
             if (MX && MODE == 1 && m == 8) read_scales(kt + 1, sa_n, sb_n);
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // MX: the scale bytes move into place for the next step here, where
+        // the waits below stall anyway (moved at the next step's start, they
+        // delayed its first MFMAs after the barrier): this step's rows 6, 7
+        // keep theirs, the next step takes the ones just read
+        if constexpr (MX && MODE == 1) {
+            // (explicit moves: as plain assignments the compiler put them
+            // back after the barrier, on the loop's back edge)
+            auto mv = [](int& dst, int src) { __asm__ volatile("v_mov_b32 %0, %1" : "=v"(dst) : "v"(src)); };
+#pragma unroll
+            for (int i = 0; i < 2; ++i) mv(sa_o[i], sa[6 + i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mv(sb_o[j], sb[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mv(sa[i], sa_n[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mv(sb[j], sb_n[j]);
         }
         // this stage fully read; the next stage of this tile landed (the next
         // tile's first stage is waited for at the top of the tile loop)

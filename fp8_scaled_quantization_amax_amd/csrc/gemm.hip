@@ -333,11 +333,13 @@ constexpr int kEpPitch32 = 528;   // bytes per staged fp32 row of 128 values (+1
 // MX (SM == kSmMx, K % 512 == 0): the E8M0 scales travel to LDS in groups of
 // four K steps: for each tile row, 16 bytes = its four 32-K blocks of four
 // consecutive K steps, one 16-byte direct-to-LDS load per lane (64 rows per
-// instruction), double-buffered by group and loaded one group ahead.  Right
-// after each barrier every lane reads the byte of its fragment rows and 32-K
-// block for all 16 fragments of the new step, and the MFMAs take them as
-// their scale operands.  The scales of the row pair that runs after the
-// barrier are kept from the previous step.
+// instruction), double-buffered by group and loaded one group ahead.  Under
+// the MFMAs of a step's rows 4, 5 every lane reads the byte of its fragment
+// rows and 32-K block for all 16 fragments of the next step (a tile's first
+// step reads its own at its start), and the MFMAs take them as their scale
+// operands.  The scales of the row pair that runs after the barrier are kept
+// from the previous step; the bytes change registers just before the
+// barrier.
 template <int FA, int FB, int OUT, int SM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pt_kernel(GemmArgs g, int ntm, int ntn) {
     constexpr bool MX = SM == kSmMx;

@@ -6,6 +6,34 @@
 // This file is compiled with MFMA results placed in VGPRs, where the FMAs
 // that add each K block's partial can read them directly (the other GEMM
 // kernels keep their accumulators in AGPRs).
+//
+// 1x128 row scales on A, and on B either 128x128 block scales (fprop / dgrad
+// weights) or 1x128 row scales (wgrad operands); K a multiple of 512.  Each
+// 16x16x128 MFMA covers exactly one 128-K block, so it runs with a zero
+// accumulator and its result is added into the fp32 accumulators with one
+// FMA per value: acc += (sA(m, kb) * sB(n, kb)) * partial.  Those FMAs need
+// the accumulators in VGPRs, so a wave owns 128 x 64 outputs (128 VGPRs).
+//  * Two waves per SIMD: eight waves over a 256 x 256 workgroup tile, two
+//    64 KB stages loaded one K step ahead by direct-to-LDS loads, the last
+//    step loading the next tile's first stage.  While one wave of a SIMD
+//    waits for a partial or issues its FMAs, the other's MFMAs keep the
+//    matrix core busy.  The first form, four waves of 128 x 64 (one per
+//    SIMD) over 256 x 128 tiles with three 48 KB stages, kept the MFMA pipes
+//    busy only 0.44 of the cycles, with about as many cycles per MFMA in
+//    which neither the MFMA nor the VALU pipe was busy as cycles of MFMA;
+//    this form ran 16% faster in the same call (wgrad 20%).
+//  * Each tile is a buffer descriptor from its first row on (scalar
+//    registers), so a lane's load offsets are fixed for the kernel and rows
+//    past the matrix read as zeros; that keeps the waves within the 256
+//    registers two waves per SIMD leave each.
+//  * Row scales travel like the MX exponents: 16 bytes per row (four K
+//    blocks) per direct-to-LDS load, one group of four K steps ahead, double
+//    buffered.  With block-scaled B the 64 columns of a wave share one scale
+//    per K block (one uniform load per step, a step ahead), so the FMA
+//    factor is one product per fragment row and step.
+//  * The FMAs of fragment row i run under the MFMAs of row i + 1.  The last
+//    row's MFMAs (and the FMAs of the last two rows) run after the next
+//    barrier, from registers, while the next step's fragments are read.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -16,39 +44,6 @@
 
 namespace fp8q {
 
-// 1x128 row scales on A, and on B either 128x128 block scales (fprop / dgrad
-// weights) or 1x128 row scales (wgrad operands); K a multiple of 512.  Each
-// 16x16x128 MFMA covers exactly one 128-K block, so it runs with a zero
-// accumulator and its result is added into the fp32 accumulators with one
-// FMA per value: acc += (sA(m, kb) * sB(n, kb)) * partial.  Those FMAs need
-// the accumulators in VGPRs, so a wave owns 128 x 64 outputs (128 VGPRs) and
-// the workgroup tile is 256 x 128.  Like the per-tensor kernel it walks
-// per-XCD tile ranges with direct-to-LDS operand loads and LDS-staged
-// row-contiguous stores with the non-temporal hint.  Its K steps are half as
-// long (32 MFMAs per wave), so it keeps three 48 KB stages and loads two steps
-// ahead; the last two K steps of a tile load the next tile's first two stages.
-//  * Row scales travel like the MX exponents: 16 bytes per row (four K
-//    blocks) per direct-to-LDS load, one group of four K steps ahead, double
-//    buffered; one 64-row load per wave per group instead of a scattered
-//    4-byte load per fragment row and step (those cost about as much as the
-//    FMAs themselves).
-//  * With block-scaled B the 64 columns of a wave share one scale per K
-//    block (one uniform load per step, a step ahead), so the FMA factor is
-//    one product per fragment row and step.
-//  * The FMAs of fragment row i run under the MFMAs of row i + 1.  The last
-//    row's MFMAs (and the FMAs of the last two rows) run after the next
-//    barrier, from registers, while the next step's fragments are read.
-//  * Where the time goes (counters): the MFMA pipes are busy 0.44 of the
-//    cycles (0.38 with row scales on both operands); the FMAs keep the VALU
-//    issuing 0.36 (0.47), half of that under a running MFMA; the LDS is far from
-//    saturated (per 1024 MFMA cycles of a K step a CU moves 96 KB of
-//    fragment reads and 48 KB of operand writes through it).  A 128 x 128
-//    wave tile would halve the operand traffic per MFMA but needs 256
-//    accumulator VGPRs, all there are; eight waves of 64 x 64, or A
-//    fragments loaded straight into registers, measured slower.  A stage's
-//    loads issued in one burst after the barrier queued behind each other
-//    and held the waves apart at every barrier (a timing copy without the
-//    barrier ran 9% faster); spread over the step they cost about 0.5%.
 // bytes spanned by a fp32 scale array (rows >> rshift, ld, kstride) over nkb K blocks
 __device__ __forceinline__ int64_t scale_bytes(const GemmScale& s, int64_t rows, int64_t nkb) {
     return ((((rows - 1) >> s.rshift) * s.ld + (nkb - 1) * s.kstride) + 1) * 4;
@@ -78,15 +73,15 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* lo, const uint8_t* hi, int
 }
 
 template <int FA, int FB, int OUT, bool BROW>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int ntm, int ntn) {
-    constexpr int BNb = 128;
-    constexpr int kStage = kTileBytes + BNb * BK;   // A 256 x 128 + B 128 x 128 bytes
+__global__ __launch_bounds__(512, 1) void gemm_bs_kernel(GemmArgs g, int ntm, int ntn) {
+    constexpr int BNb = 256;
+    constexpr int kStage = kTileBytes + BNb * BK;   // A 256 x 128 + B 256 x 128 bytes
     constexpr int kScA = BM * 16, kScGroup = kScA + (BROW ? BNb * 16 : 0);
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[3 * kStage + 2 * kScGroup];
-    uint8_t* const lds_sc = lds_all + 3 * kStage;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[2 * kStage + 2 * kScGroup];
+    uint8_t* const lds_sc = lds_all + 2 * kStage;
     const int64_t M = g.M, N = g.N, K = g.K;
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
-    const int wm = (w >> 1) * 128, wn = (w & 1) * 64;
+    const int wm = (w >> 2) * 128, wn = (w & 3) * 64;
     const FragLane fa = frag_lane(wm), fb = frag_lane(wn);
     constexpr int kFmtA = FA == FP8Q_E4M3 ? 0 : 1;
     constexpr int kFmtB = FB == FP8Q_E4M3 ? 0 : 1;
@@ -99,79 +94,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
     const int ngroups = nk / 4;
     const int wave = __builtin_amdgcn_readfirstlane(w);
     const uint32_t K32 = (uint32_t)K;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.A, M * K), rb = buffer_rsrc(g.B, N * K);
-    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(g.sa.s, scale_bytes(g.sa, M, nk));
     const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(g.sb.s, scale_bytes(g.sb, N, nk));
     const uint32_t lda4 = (uint32_t)(g.sa.ld * 4), ldb4 = (uint32_t)(g.sb.ld * 4);
     const uint32_t ksb4 = (uint32_t)(g.sb.kstride * 4);
+    // the scale rows a wave stages: waves 0-3 A rows 64 (wave % 4) + lane;
+    // waves 4-7 the same rows of B (row-scaled B) or of A again (the same
+    // bytes to the same place), so every wave issues one load per group
+    const bool gb = BROW && wave >= 4;
+    const int sc_dst = (gb ? kScA : 0) + (wave & 3) * 64 * 16;
+    // Offsets relative to the tile's first row, fixed for the kernel: a
+    // wave loads rows 32 wave + l / 8 (+ 8 u) of both operand tiles, and its
+    // scale row; the tile itself is a buffer descriptor over its first row
+    // onwards (scalar registers), whose end turns rows past the matrix into zeros.
+    const DmaB dl = dmab_rows(K, 32 * wave);
+    const uint32_t sg_lane = (uint32_t)(64 * (wave & 3) + l) * (gb ? ldb4 : lda4);
 
-    // per-tile state: DMA plans; byte offsets of the scale rows this wave
-    // stages (A rows 64 wave + lane; B rows likewise, waves 0 and 1), or of
-    // the wave's B block scale for K block 0
     struct TileState {
-        DmaB a, b;
-        uint32_t sa_row, sb_row;
+        __amdgpu_buffer_rsrc_t ra, rb, rs;   // the tile's rows of A, of B, of the staged scales
+        uint32_t sb_blk;                     // block-scaled B: the wave's B block scale for K block 0
     };
     auto tile_state = [&](int lg) {
         int tm, tn;
         tile_coords(lg, ntm, ntn, tm, tn);
         const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNb;
         TileState s;
-        s.a = dmab_rows(K, m0 + 64 * wave);
-        s.b = dmab_rows(K, n0 + 32 * wave);
-        s.sa_row = (uint32_t)(m0 + 64 * wave + l) * lda4;
-        if constexpr (BROW) {
-            s.sb_row = (uint32_t)(n0 + 64 * wave + l) * ldb4;
-        } else {
+        s.ra = buffer_rsrc(g.A + m0 * K, (M - m0) * K);
+        s.rb = buffer_rsrc(g.B + n0 * K, (N - n0) * K);
+        s.rs = gb ? buffer_rsrc(reinterpret_cast<const float*>(g.sb.s) + n0 * g.sb.ld, scale_bytes(g.sb, N - n0, nk))
+                  : buffer_rsrc(reinterpret_cast<const float*>(g.sa.s) + m0 * g.sa.ld, scale_bytes(g.sa, M - m0, nk));
+        s.sb_blk = 0;
+        if constexpr (!BROW) {
             const int64_t nb = (n0 + wn) >> 7, nb_last = (N - 1) >> 7;
-            s.sb_row = (uint32_t)(nb < nb_last ? nb : nb_last) * ldb4;
+            s.sb_blk = (uint32_t)(nb < nb_last ? nb : nb_last) * ldb4;
         }
         return s;
     };
-    // load instruction u (0..11) of a stage: 8 of A rows, then 4 of B rows
+    // load instruction u (0..7) of a stage: 4 of A rows, then 4 of B rows
     auto stage_load = [&](const TileState& s, uint32_t ko, uint8_t* dst, int u) {
-        if (u < 8)
-            dma_one(ra, ((u & 1) ? s.a.o : s.a.e) + (uint32_t)(u * 8) * K32 + ko, 0u, dst + (wave * 64 + u * 8) * BK);
-        else
-            dma_one(rb, (((u - 8) & 1) ? s.b.o : s.b.e) + (uint32_t)((u - 8) * 8) * K32 + ko, 0u,
-                    dst + kTileBytes + (wave * 32 + (u - 8) * 8) * BK);
+        const uint32_t off = (((u & 1) ? dl.o : dl.e) + (uint32_t)((u & 3) * 8) * K32) + ko;
+        if (u < 4) dma_one(s.ra, off, 0u, dst + (wave * 32 + u * 8) * BK);
+        else dma_one(s.rb, off, 0u, dst + kTileBytes + (wave * 32 + (u - 4) * 8) * BK);
     };
-    // scale group gi (K blocks 4 gi .. 4 gi + 3: 16 bytes per row) into buffer buf
     auto group_load = [&](const TileState& s, int buf, int gi) {
-        uint8_t* dst = lds_sc + buf * kScGroup;
-        dma_one(rsa, s.sa_row + (uint32_t)gi * 16, 0u, dst + wave * 64 * 16);
-        if constexpr (BROW) {
-            if (wave < 2) dma_one(rsb, s.sb_row + (uint32_t)gi * 16, 0u, dst + kScA + wave * 64 * 16);
-        }
+        dma_one(s.rs, sg_lane + (uint32_t)gi * 16, 0u, lds_sc + buf * kScGroup + sc_dst);
     };
-    float sbn = 0.f;   // block-scaled B: the wave's scale of the next K step
+    float sbn = 0.f;
 
     TileState cur = tile_state(logical);
-    // stage 0, the first scale group (and B block scale), then stage 1: the
-    // wait at the top of a step leaves only the 12 loads of the following
-    // stage in flight
 #pragma unroll
-    for (int u = 0; u < 12; ++u) stage_load(cur, 0u, lds_all, u);
+    for (int u = 0; u < 8; ++u) stage_load(cur, 0u, lds_all, u);
     group_load(cur, 0, 0);
-    if constexpr (!BROW) sbn = load_f32(rsb, cur.sb_row);
-#pragma unroll
-    for (int u = 0; u < 12; ++u) stage_load(cur, (uint32_t)BK, lds_all + kStage, u);
+    if constexpr (!BROW) sbn = load_f32(rsb, cur.sb_blk);
 
     constexpr int NSB = BROW ? 16 : 1;
     v4f acc[8][4];
-    // p: the MFMA partials of fragment rows of parity 0 / 1
     v4f p[2][4];
     v8i b[4], a[2];
-    // FMA factors: sf[i] for fragment row i, the A row scale times the B
-    // block scale (or the A row scale alone, times the B row scales sbr per
-    // value); sraw / sbc: the step's scales as read
     float sf[8], sbr[NSB], sraw[8];
-    int par = 0, gpar = 0;   // buffers (of 3 / of 2) holding the tile's stage 0 / first scale group
+    int par = 0, gpar = 0;   // buffers (of 2) holding the tile's stage 0 / first scale group
     while (true) {
         const int next = logical + per;
         const bool has_next = next < hi;
-        // without a next tile the last two steps re-load this tile's first
-        // stages into free buffers: harmless, and it keeps the steps branch-free
         const TileState nxt = tile_state(has_next ? next : logical);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -186,56 +169,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
             for (int r = 0; r < 4; ++r)
                 acc[i][j][r] = __builtin_fmaf(p[i & 1][j][r], BROW ? sf[i] * sbr[4 * j + r] : sf[i], acc[i][j][r]);
         };
-        // One K step.  Stage kt sits in buffer (par + kt) % 3; the step loads
-        // stage kt + 2 (of this tile, or the next tile's stage kt + 2 - nk)
-        // into the buffer every wave finished with before the barrier, two
-        // loads under each of fragment rows 1-6 (a tile's first step, with no
-        // rows of the previous step to run, issues them at once).  With
-        // DEF the previous step's fragment row 7 is still open: its MFMAs run
-        // first, straight after the barrier and from registers only, while
-        // this step's fragments are read; its FMAs follow under row 0's MFMAs.
-        // Row i's FMAs run under row i + 1's MFMAs, whose partial they do not
-        // touch; row i + 1's A fragment is read into the registers row i - 1
-        // used.  The scheduling barriers keep this order (left free, the
-        // compiler put each FMA group right behind the MFMA producing it).
+        // One K step: stage kt sits in buffer (par + kt) % 2; the step loads
+        // stage kt + 1 (or the next tile's stage 0) into the other buffer,
+        // which every wave finished reading before the barrier (a tile's
+        // first step, with no rows of the previous step to run, issues the
+        // loads at once).  With DEF the previous step's fragment row 7 is
+        // still open: its MFMAs run first, straight after the barrier and
+        // from registers only, while this step's fragments are read; its
+        // FMAs follow under row 0's MFMAs.  Row i's FMAs run under row
+        // i + 1's MFMAs, whose partial they do not touch; row i + 1's A
+        // fragment is read into the registers row i - 1 used.  The
+        // scheduling barriers keep this order (left free, the compiler put
+        // each FMA group right behind the MFMA producing it).
         auto step = [&](auto def_c, int kt) {
             constexpr bool DEF = decltype(def_c)::value;
-            // this stage, its scales and the B block scale landed; every wave
-            // is done with the buffer the loads below overwrite
-            vm_wait<12>();
+            // this stage, its scale group and the B block scale landed;
+            // every wave is done with the buffer the loads below overwrite
+            vm_wait<0>();
             stage_barrier();
-            const bool last = kt + 1 == nk, next2 = kt + 2 >= nk;
+            const bool last = kt + 1 == nk;
             const int gi = kt >> 2;
-            // scale groups: the next one of this tile at a group's first step,
-            // the next tile's first one at the last step
             if (last) group_load(nxt, (ngroups + gpar) & 1, 0);
             else if ((kt & 3) == 0 && gi + 1 < ngroups) group_load(cur, (gi + 1 + gpar) & 1, gi + 1);
             float sbc = 0.f;
             if constexpr (!BROW) {
                 sbc = sbn;
-                sbn = load_f32(rsb, last ? nxt.sb_row : cur.sb_row + (uint32_t)(kt + 1) * ksb4);
+                sbn = load_f32(rsb, last ? nxt.sb_blk : cur.sb_blk + (uint32_t)(kt + 1) * ksb4);
             }
             TileState ld;   // field by field: a selected reference would live in scratch memory
-            ld.a.e = next2 ? nxt.a.e : cur.a.e;
-            ld.a.o = next2 ? nxt.a.o : cur.a.o;
-            ld.b.e = next2 ? nxt.b.e : cur.b.e;
-            ld.b.o = next2 ? nxt.b.o : cur.b.o;
-            const uint32_t ko = (uint32_t)(next2 ? kt + 2 - nk : kt + 2) * BK;
-            const uint8_t* la = lds_all + ((par + kt) % 3) * kStage;
+            ld.ra = last ? nxt.ra : cur.ra;
+            ld.rb = last ? nxt.rb : cur.rb;
+            const uint32_t ko = (uint32_t)(last ? 0 : kt + 1) * BK;
+            const uint8_t* la = lds_all + ((par + kt) & 1) * kStage;
             const uint8_t* lb = la + kTileBytes;
-            uint8_t* dst = lds_all + ((par + kt + 2) % 3) * kStage;
+            uint8_t* dst = lds_all + ((par + kt + 1) & 1) * kStage;
             const uint8_t* gs = lds_sc + ((gi + gpar) & 1) * kScGroup + 4 * (kt & 3);
-            // per-lane fragment bases of this stage (rows wm + 16 i of A, wn + 16 j of B)
             const uint8_t* alo = la + fa.lo;
             const uint8_t* ahi = la + fa.hi;
             const uint8_t* blo = lb + fb.lo;
             const uint8_t* bhi = lb + fb.hi;
-            // scale rows of fragment row 0 / column fragment 0, read as integers: read
-            // as float, the compiler could not tell them from the direct-to-LDS
-            // loads in flight and waited for all of them
             const uint8_t* gsa = gs + (wm + (l & 15)) * 16;
             const uint8_t* gsb = gs + kScA + (wn + 4 * (l >> 4)) * 16;
 
+            // the next stage's eight loads, two under each of the first four
+            // fragment rows the step runs (the previous step's row 7 - row
+            // -1 here - then rows 0-2): issued later they landed too late for
+            // the next step, all under row 7 they queued behind each other
+            auto spread_load = [&](int i, int j) {
+                if (DEF && i <= 2 && (j & 1)) stage_load(ld, ko, dst, 2 * (i + 1) + (j >> 1));
+            };
             __builtin_amdgcn_sched_barrier(0);
             a[0] = frag_at(alo, ahi, 0);
             if constexpr (DEF) {
@@ -243,6 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                 for (int j = 0; j < 4; ++j) {
                     mfma_one(7, j);
                     b[j] = frag_at(blo, bhi, j);
+                    spread_load(-1, j);
                     fma_one(6, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -250,21 +233,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
 #pragma unroll
                 for (int j = 0; j < 4; ++j) b[j] = frag_at(blo, bhi, j);
 #pragma unroll
-                for (int u = 0; u < 12; ++u) stage_load(ld, ko, dst, u);
+                for (int u = 0; u < 8; ++u) stage_load(ld, ko, dst, u);
             }
             a[1] = frag_at(alo, ahi, 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 mfma_one(0, j);
+                spread_load(0, j);
                 if constexpr (DEF) fma_one(7, j);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // this step's scales, after the last use of the previous step's;
-            // row i's factor is formed where its FMAs start, so that no
-            // instruction waits for these reads before it must
+            // row scales: rows 0 and 1 here, row i + 1 under row i's MFMAs
+            // (a few live registers rather than all eight)
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 2; ++i)
                 sraw[i] = __uint_as_float(*reinterpret_cast<const uint32_t*>(gsa + 16 * i * 16));
             if constexpr (BROW) {
 #pragma unroll
@@ -279,27 +262,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
                     mfma_one(i, j);
                     if (j == 0) {
                         a[(i + 1) & 1] = frag_at(alo, ahi, i + 1);
+                        sraw[i + 1] = __uint_as_float(*reinterpret_cast<const uint32_t*>(gsa + 16 * (i + 1) * 16));
                         sf[i - 1] = BROW ? sraw[i - 1] : sraw[i - 1] * sbc;
                     }
-                    // the next stages' loads, two per fragment row: issued all at
-                    // once after the barrier they queued behind each other and
-                    // held the waves apart at every barrier (+6.5%, wgrad +13-20%)
-                    if (DEF && (j & 1)) stage_load(ld, ko, dst, 2 * (i - 1) + (j >> 1));
+                    spread_load(i, j);
                     fma_one(i - 1, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
 #pragma unroll
             for (int i = 6; i < 8; ++i) sf[i] = BROW ? sraw[i] : sraw[i] * sbc;
-            // every read of this stage has returned before the barrier that
-            // frees its buffer
             lds_wait_all();
         };
         using T = std::true_type;
         using F = std::false_type;
         step(F{}, 0);
         for (int kt = 1; kt < nk; ++kt) step(T{}, kt);
-        // the last step's row 7
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             mfma_one(7, j);
@@ -313,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
         int tm, tn;
         tile_coords(logical, ntm, ntn, tm, tn);
         const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNb;
-        uint8_t* ep0 = lds_all + ((par + nk - 1) % 3) * kStage;
+        uint8_t* ep0 = lds_all + ((par + nk - 1) & 1) * kStage;
         if constexpr (OUT == FP8Q_BF16) {
             typedef float v2f_t __attribute__((ext_vector_type(2)));
             typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
@@ -363,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
         }
         if (!has_next) break;
         logical = next;
-        par = (par + nk) % 3;
+        par = (par + nk) & 1;
         gpar = (ngroups + gpar) & 1;
         cur = nxt;
     }
@@ -371,15 +349,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bs_kernel(GemmArgs g, int nt
     vm_wait<0>();
 }
 
-
 template <int FA, int FB, int OUT>
 static void launch_out(const GemmArgs& g, hipStream_t s) {
-    const int ntm = (int)((g.M + BM - 1) / BM), ntn = (int)((g.N + 127) / 128);
+    const int ntm = (int)((g.M + BM - 1) / BM), ntn = (int)((g.N + 255) / 256);
     if (g.sb.rshift == 0)
-        hipLaunchKernelGGL((gemm_bs_kernel<FA, FB, OUT, true>), dim3(persistent_grid()), dim3(kThreads), 0, s, g, ntm,
+        hipLaunchKernelGGL((gemm_bs_kernel<FA, FB, OUT, true>), dim3(persistent_grid()), dim3(512), 0, s, g, ntm,
                            ntn);
     else
-        hipLaunchKernelGGL((gemm_bs_kernel<FA, FB, OUT, false>), dim3(persistent_grid()), dim3(kThreads), 0, s, g,
+        hipLaunchKernelGGL((gemm_bs_kernel<FA, FB, OUT, false>), dim3(persistent_grid()), dim3(512), 0, s, g,
                            ntm, ntn);
 }
 

@@ -78,6 +78,55 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_graph_replays_granular_and_autocast_gemms():
+    """The persistent block-scaled GEMM (128x128-block B on fprop, row scales
+    on both wgrad operands), the MX32 GEMM and an autocast GEMM (amax grid,
+    cast and completion counters in its workspace), captured in one graph and
+    replayed three times with eager library calls in between: every replay
+    equals the eager results bitwise."""
+    from test_gpu_gemm import block_scaled_codes, mx_codes
+    announce("graph replay: block-scaled, MX and autocast GEMMs")
+    M, N, K = 528, 400, 1024   # K % 512 == 0: the persistent granular kernels
+    A, B = inputs()
+    At, Bt = workloads.gemm_operands("TN", M, N, K, seed=511, std=1.0, outlier_rows=0.01)
+    ba, bb = block_scaled_codes("NT", A, B, fq.E4M3, fq.E4M3)[:2]
+    ta, tb = block_scaled_codes("TN", At, Bt, fq.E5M2, fq.E4M3)[:2]
+    ma, mb = mx_codes("NT", A, B, fq.E4M3, fq.E4M3)[:2]
+    need = fq.gemm_workspace_bytes("NT", M, N, K, AC(A, fq.E4M3), AC(B, fq.E4M3))
+    ws = fq._ws(need, dev())
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev()) for _ in range(4)]
+
+    def work():
+        fq.fp8_gemm_scaled_NT(M, N, K, ba, bb, torch.bfloat16, out=outs[0])
+        fq.fp8_gemm_scaled_TN(M, N, K, ta, tb, torch.bfloat16, out=outs[1])
+        fq.fp8_gemm_scaled_NT(M, N, K, ma, mb, torch.bfloat16, out=outs[2])
+        fq.fp8_gemm_scaled_NT(M, N, K, AC(A, fq.E4M3), AC(B, fq.E4M3), torch.bfloat16, out=outs[3], ws=ws)
+
+    work()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    s = torch.cuda.Stream(device=dev())
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    other = workloads.normal((256, 512), 4.0, 512, torch.bfloat16).to(dev())
+    for replay in range(3):
+        for o in outs:
+            o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), (replay, k)
+        fq.fp8_gemm_scaled_NT(256, 256, 512, AC(other[:, :512], fq.E5M2), AC(other[:256], fq.E4M3),
+                              torch.bfloat16)   # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_delayed_scaling_replayed_graph_follows_the_oracle():
     """The delayed state lives in device memory, so one captured delayed cast,
     replayed once per step with that step's data copied into its input

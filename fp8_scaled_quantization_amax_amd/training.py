@@ -89,10 +89,12 @@ class FP8MatmulRowwise(torch.autograd.Function):
     - dgrad NN: dy per row, w per column (its K-major copy);
     - wgrad TN: dy and x per column (K-major copies).
 
-    Each product is sum_k qa qb * sA[m] * sB[n]."""
+    Each product is sum_k qa qb * sA[m] * sB[n].  With gw_hp (the page's
+    "rowwise_with_gw_hp" recipe) the wgrad GEMM is not quantized: dw = dy^T x
+    in the inputs' own precision (torch's matmul), fprop and dgrad as above."""
 
     @staticmethod
-    def forward(ctx, x, w):
+    def forward(ctx, x, w, gw_hp=False):
         if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
             raise ValueError(f"FP8MatmulRowwise needs x[M,K] and w[N,K], got {tuple(x.shape)} and {tuple(w.shape)}")
         if x.dtype != w.dtype or x.dtype not in (torch.float32, torch.bfloat16):
@@ -105,14 +107,16 @@ class FP8MatmulRowwise(torch.autograd.Function):
         y = fp8_gemm_scaled_NT(M, N, K, GemmOperand.quantized(qx, E4M3, sx, ROWWISE),
                                GemmOperand.quantized(qw, E4M3, sw, ROWWISE), x.dtype)
         saved = []
-        if ctx.needs_input_grad[1]:    # wgrad: x per column (over tokens)
+        if ctx.needs_input_grad[1] and gw_hp:   # wgrad in high precision: x itself
+            saved += [x]
+        elif ctx.needs_input_grad[1]:    # wgrad: x per column (over tokens)
             qx1, qx1T, sx1 = fp8_quantize_rowwise(x, 1, E4M3, emit_t=True)
             saved += [qx1, qx1T, sx1]
         if ctx.needs_input_grad[0]:    # dgrad: w per column (over output features)
             qw1, qw1T, sw1 = fp8_quantize_rowwise(w, 1, E4M3, emit_t=True)
             saved += [qw1, qw1T, sw1]
         ctx.save_for_backward(*saved)
-        ctx.dtype, ctx.shape = x.dtype, (M, N, K)
+        ctx.dtype, ctx.shape, ctx.gw_hp = x.dtype, (M, N, K), gw_hp
         return y
 
     @staticmethod
@@ -121,7 +125,11 @@ class FP8MatmulRowwise(torch.autograd.Function):
         saved = list(ctx.saved_tensors)
         dy = dy.to(ctx.dtype).contiguous()
         dx = dw = None
-        if ctx.needs_input_grad[1]:
+        if ctx.needs_input_grad[1] and ctx.gw_hp:
+            x = saved[0]
+            saved = saved[1:]
+            dw = dy.t().contiguous() @ x
+        elif ctx.needs_input_grad[1]:
             qx1, qx1T, sx1 = saved[:3]
             saved = saved[3:]
             qg1, qg1T, sg1 = fp8_quantize_rowwise(dy, 1, E5M2, emit_t=True)
@@ -132,17 +140,18 @@ class FP8MatmulRowwise(torch.autograd.Function):
             qg0, _, sg0 = fp8_quantize_rowwise(dy, 0, E5M2)
             dx = fp8_gemm_scaled_NN(M, K, N, GemmOperand.quantized(qg0, E5M2, sg0, ROWWISE),
                                     GemmOperand.quantized(qw1, E4M3, sw1, ROWWISE, kmajor=qw1T), ctx.dtype)
-        return dx, dw
+        return dx, dw, None
 
 
 def fp8_matmul(x, w, recipe="tensorwise", sr=None, rht=None):
     """x . w^T through FP8Matmul ("tensorwise", optionally with stochastically
     rounded gradients, sr = (seed, offset), and a Hadamard-transformed wgrad,
-    rht = seed) or FP8MatmulRowwise ("rowwise")."""
-    if recipe == "rowwise":
+    rht = seed) or FP8MatmulRowwise ("rowwise", or "rowwise_with_gw_hp" with
+    the wgrad GEMM in high precision)."""
+    if recipe in ("rowwise", "rowwise_with_gw_hp"):
         if sr is not None or rht is not None:
             raise ValueError("stochastic rounding and the Hadamard transform are implemented for the tensorwise recipe")
-        return FP8MatmulRowwise.apply(x, w)
+        return FP8MatmulRowwise.apply(x, w, recipe == "rowwise_with_gw_hp")
     if recipe != "tensorwise":
         raise ValueError(f"unknown recipe {recipe!r}")
     return FP8Matmul.apply(x, w, sr, rht)

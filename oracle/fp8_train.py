@@ -65,15 +65,18 @@ def _qr(t, fmt, axis, K):
 class OracleFP8MatmulRowwise(torch.autograd.Function):
     """The "rowwise" recipe: each GEMM input scaled per row along that GEMM's
     contraction (x, w per row for fprop; dy per row and w per column for
-    dgrad; dy and x per column for wgrad)."""
+    dgrad; dy and x per column for wgrad).  gw_hp: the "rowwise_with_gw_hp"
+    recipe, whose wgrad is not quantized: dw = dy^T x of the unquantized
+    values, in fp64, rounded once to fp32."""
 
     @staticmethod
-    def forward(ctx, x, w):
+    def forward(ctx, x, w, gw_hp=False):
         M, K = x.shape
         N = w.shape[0]
         qx, sx = _qr(x, E4M3, 0, K)
         qw, sw = _qr(w, E4M3, 0, K)
         ctx.saved = (x.detach().clone(), w.detach().clone())
+        ctx.gw_hp = gw_hp
         return torch.from_numpy(gemm_nt(qx, qw, E4M3, E4M3, sx, sw).astype(np.float32))
 
     @staticmethod
@@ -84,10 +87,13 @@ class OracleFP8MatmulRowwise(torch.autograd.Function):
         qg0, sg0 = _qr(dy, E5M2, 0, N)
         qw1, sw1 = _qr(w, E4M3, 1, N)
         dx = torch.from_numpy(gemm_nn(qg0, qw1, E5M2, E4M3, sg0, sw1).astype(np.float32))
-        qg1, sg1 = _qr(dy, E5M2, 1, M)
-        qx1, sx1 = _qr(x, E4M3, 1, M)
-        dw = torch.from_numpy(gemm_tn(qg1, qx1, E5M2, E4M3, sg1, sx1).astype(np.float32))
-        return dx, dw
+        if ctx.gw_hp:
+            dw = torch.from_numpy((dy.detach().double().numpy().T @ x.double().numpy()).astype(np.float32))
+        else:
+            qg1, sg1 = _qr(dy, E5M2, 1, M)
+            qx1, sx1 = _qr(x, E4M3, 1, M)
+            dw = torch.from_numpy(gemm_tn(qg1, qx1, E5M2, E4M3, sg1, sx1).astype(np.float32))
+        return dx, dw, None
 
 
 def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", grad_sr_seed=None,
@@ -101,8 +107,8 @@ def train_mlp(X, Y, W1, W2, fp8=True, steps=300, lr=3e-3, recipe="tensorwise", g
 
     def fp8_mm(t):
         def mm(a, b, j):
-            if recipe == "rowwise":
-                return OracleFP8MatmulRowwise.apply(a, b)
+            if recipe in ("rowwise", "rowwise_with_gw_hp"):
+                return OracleFP8MatmulRowwise.apply(a, b, recipe == "rowwise_with_gw_hp")
             return OracleFP8Matmul.apply(a, b, None if grad_sr_seed is None else (grad_sr_seed, 2 * t + j),
                                          None if wgrad_rht_seed is None else wgrad_rht_seed + 2 * t + j)
         return mm

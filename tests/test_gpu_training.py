@@ -156,6 +156,42 @@ def test_rowwise_training_parity(training, lab):
     assert rel.max() < 0.05
 
 
+def test_rowwise_gw_hp_one_step_matches_oracle(training, lab):
+    """The rowwise_with_gw_hp recipe (wgrad not quantized): forward output and
+    both gradients agree with the oracle's (fp32 tolerance)."""
+    dev = torch.device("cuda")
+    h = torch.relu(lab["X"] @ lab["W1"].T)
+    g = torch.randn(512, 16, generator=torch.Generator().manual_seed(8)) * 1e-3
+    xo, wo = h.clone().requires_grad_(), lab["W2"].clone().requires_grad_()
+    yo = fp8_train.OracleFP8MatmulRowwise.apply(xo, wo, True)
+    yo.backward(g)
+    xg, wg = h.to(dev).requires_grad_(), lab["W2"].to(dev).requires_grad_()
+    yg = training.fp8_matmul(xg, wg, "rowwise_with_gw_hp")
+    yg.backward(g.to(dev))
+    torch.cuda.synchronize()
+    _close(yg, yo, "y")
+    _close(xg.grad, xo.grad, "dx")
+    _close(wg.grad, wo.grad, "dw")
+
+
+def test_rowwise_gw_hp_training_parity(training, lab):
+    """Check [5]'s bound on the GPU with the rowwise_with_gw_hp recipe, and the
+    loss curve against the oracle's run (step 0 to the GEMM tolerance, the
+    curve within 5%)."""
+    dev = torch.device("cuda")
+    X, Y, W1, W2 = (lab[k].to(dev) for k in ("X", "Y", "W1", "W2"))
+    l8 = training.train_mlp(X, Y, W1, W2, fp8=True, recipe="rowwise_with_gw_hp")
+    l32 = training.train_mlp(X, Y, W1, W2, fp8=False)
+    o8 = fp8_train.train_mlp(lab["X"], lab["Y"], lab["W1"], lab["W2"], fp8=True, recipe="rowwise_with_gw_hp")
+    gap = abs(l8[-1] - l32[-1]) / l32[-1]
+    rel = np.abs(np.array(l8) - np.array(o8)) / np.array(o8)
+    print(f"rowwise_with_gw_hp: final loss fp32 {l32[-1]:.6f}, FP8 GPU {l8[-1]:.6f}, FP8 oracle {o8[-1]:.6f}; "
+          f"gap {100 * gap:.2f}%; GPU vs oracle step 0 {rel[0]:.2e}, all {rel.max():.2e}", flush=True)
+    assert gap < 0.10
+    assert rel[0] <= TOL_F32
+    assert rel.max() < 0.05
+
+
 def test_sr_gradient_one_step_matches_oracle(training, lab):
     """Stochastically rounded output gradient (same seed and offset on both
     sides, so the same codes): forward output and both gradients agree with

@@ -99,6 +99,36 @@ def test_rowwise_lab_check5_final_loss_gap():
     assert lr[-1] < 0.5 * lr[0]
 
 
+def test_rowwise_gw_hp_one_step():
+    """The rowwise_with_gw_hp recipe: y and dx exactly as in the rowwise
+    recipe, and dw equal to torch's own fp32 autograd gradient of x . w^T
+    (the wgrad GEMM is not quantized)."""
+    d = workloads.lab_mlp_inputs()
+    x = torch.relu(d["X"] @ d["W1"].T)
+    g = torch.randn(512, 16, generator=torch.Generator().manual_seed(5)) * 1e-3
+    xr, wr = x.clone().requires_grad_(), d["W2"].clone().requires_grad_()
+    yr = fp8_train.OracleFP8MatmulRowwise.apply(xr, wr)
+    yr.backward(g)
+    xh, wh = x.clone().requires_grad_(), d["W2"].clone().requires_grad_()
+    yh = fp8_train.OracleFP8MatmulRowwise.apply(xh, wh, True)
+    yh.backward(g)
+    assert torch.equal(yh, yr) and torch.equal(xh.grad, xr.grad)
+    xt, wt = x.clone().requires_grad_(), d["W2"].clone().requires_grad_()
+    (xt @ wt.T).backward(g)
+    err = (wh.grad.double() - wt.grad.double()).abs().max().item()
+    assert err <= 1e-6 * wt.grad.abs().max().item(), err
+    assert not torch.equal(wh.grad, wr.grad)   # the quantized wgrad differs
+
+
+def test_rowwise_gw_hp_lab_check5_final_loss_gap():
+    """Check [5]'s bound applied to the rowwise_with_gw_hp recipe."""
+    d = workloads.lab_mlp_inputs()
+    l32 = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=False)
+    lh = fp8_train.train_mlp(d["X"], d["Y"], d["W1"], d["W2"], fp8=True, recipe="rowwise_with_gw_hp")
+    assert abs(lh[-1] - l32[-1]) / l32[-1] < 0.10
+    assert lh[-1] < 0.5 * lh[0]
+
+
 def test_sr_gradients_lab_check5_final_loss_gap():
     """Check [5]'s bound with stochastically rounded E5M2 gradients."""
     d = workloads.lab_mlp_inputs()
